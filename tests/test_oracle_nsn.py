@@ -1,0 +1,284 @@
+"""Pins for the oracle's NSN, Hadamard, VQ and (de)quantize steps.
+
+Each test checks the oracle against something other than itself: a library
+routine, a closed form, an invariant the pages state, a textbook special
+case, or brute force by explicit loops.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+import synth
+
+D = 128
+
+
+# --- Hadamard rotation (NSNQuant summary, Methodology §2) -------------------
+
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_sylvester_matches_scipy_and_is_orthogonal(d):
+    H = oracle.hadamard_matrix(d)
+    # scipy.linalg.hadamard builds the Sylvester construction in natural order
+    assert np.array_equal(H, scipy.linalg.hadamard(d).astype(np.float64))
+    assert np.array_equal(H @ H.T, d * np.eye(d))
+
+
+def test_hadamard_entry_formula():
+    H = oracle.hadamard_matrix(D)
+    i, j = np.meshgrid(np.arange(D), np.arange(D), indexing="ij")
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i & j)
+    assert np.array_equal(H, (-1.0) ** pc)
+
+
+def test_rotate_is_orthonormal_involution():
+    rng = np.random.default_rng(1)
+    u = rng.standard_normal((7, D))
+    r = oracle.rotate(u)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=1), np.linalg.norm(u, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(oracle.rotate(r), u, atol=1e-13)
+    # against scipy's matrix, applied directly
+    np.testing.assert_allclose(r, u @ scipy.linalg.hadamard(D) / np.sqrt(D), atol=1e-13)
+
+
+def test_rotate_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        oracle.hadamard_matrix(96)
+
+
+# --- NSN (NSNQuant summary, Methodology §1) ---------------------------------
+
+def _seq(T=512, seed=3, scale=5.0):
+    K, _ = synth.kv_numpy(1, T, scale, seed=seed, dtype=np.float32)
+    return K[0].astype(np.float64)
+
+
+def test_normalize_gives_norm_sqrt_d_and_restores():
+    x = _seq()
+    y, s = oracle.normalize_tokens(x)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.sqrt(D), rtol=1e-12)
+    np.testing.assert_allclose(s[:, None] * y, x, rtol=1e-12, atol=1e-12)
+    # s is the RMS of the token
+    np.testing.assert_allclose(s, np.sqrt(np.mean(x * x, axis=1)), rtol=1e-12)
+
+
+def test_normalize_zero_token_and_scale_invariance():
+    x = _seq(T=8)
+    x[3] = 0.0
+    y, s = oracle.normalize_tokens(x)
+    assert s[3] == 0.0 and np.all(y[3] == 0.0)
+    y2, s2 = oracle.normalize_tokens(x * 7.25)
+    np.testing.assert_allclose(y2, y, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s2, 7.25 * s, rtol=1e-13)
+
+
+@pytest.mark.parametrize("G", [128, 256])
+def test_shift_zero_channel_means_per_group(G):
+    x = _seq(T=512)
+    y, _ = oracle.normalize_tokens(x)
+    z, o = oracle.shift_channels(y, G)
+    sums = z.reshape(-1, G, D).sum(axis=1)
+    assert np.abs(sums).max() < 1e-12 * np.sqrt(D) * G
+    # o is a plain per-group per-channel average
+    for g in range(512 // G):
+        np.testing.assert_allclose(o[g], y[g * G:(g + 1) * G].sum(0) / G, rtol=1e-13, atol=1e-15)
+
+
+def test_shift_rejects_partial_group():
+    with pytest.raises(ValueError):
+        oracle.shift_channels(np.zeros((100, D)), 128)
+
+
+def test_nsn_norms_reconstruction_and_permutation():
+    G = 128
+    x = _seq(T=256)
+    u, s1, o, s2 = oracle.nsn(x, G)
+    np.testing.assert_allclose(np.linalg.norm(u, axis=1), np.sqrt(D), rtol=1e-12)
+    np.testing.assert_allclose(s1[:, None] * (s2[:, None] * u + np.repeat(o, G, 0)), x,
+                               rtol=1e-11, atol=1e-11)
+    # permuting tokens inside a group permutes outputs, leaves o unchanged
+    perm = np.arange(256)
+    rng = np.random.default_rng(5)
+    perm[:G] = rng.permutation(G)
+    up, s1p, op, s2p = oracle.nsn(x[perm], G)
+    np.testing.assert_allclose(up, u[perm], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(op, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s2p, s2[perm], rtol=1e-12)
+
+
+def test_nsn_commutes_with_rotation():
+    """NSN(R x) = R NSN(x) with s1, s2 unchanged and o -> R o (R orthonormal)."""
+    G = 128
+    x = _seq(T=256)
+    u, s1, o, s2 = oracle.nsn(x, G)
+    ur, s1r, or_, s2r = oracle.nsn(oracle.rotate(x), G)
+    np.testing.assert_allclose(ur, oracle.rotate(u), atol=1e-11)
+    np.testing.assert_allclose(s1r, s1, rtol=1e-12)
+    np.testing.assert_allclose(s2r, s2, rtol=1e-11)
+    np.testing.assert_allclose(or_, oracle.rotate(o), atol=1e-12)
+
+
+def _moments(a):
+    mu = a.mean(0)
+    var = a.var(0)
+    c = a - mu
+    return (np.abs(mu).max(), np.abs(var - 1).max(),
+            np.abs((c ** 3).mean(0) / var ** 1.5).max(),
+            np.abs((c ** 4).mean(0) / var ** 2 - 3).max())
+
+
+def test_nsn_plus_hadamard_output_approaches_standard_normal():
+    """README Overview / summary §1: NSN with the Hadamard transform aligns the
+    KV distribution with N(0,1).  On 65536 outlier-model key tokens the
+    per-channel moments of h are close to N(0,1); the raw keys are far."""
+    K, V = synth.kv_numpy(16, 4096, 5.0, seed=11)
+    hk = np.concatenate([oracle.rotate(oracle.nsn(K[s].astype(np.float64), 128)[0])
+                         for s in range(16)])
+    hv = np.concatenate([oracle.rotate(oracle.nsn(V[s].astype(np.float64), 128)[0])
+                         for s in range(16)])
+    # pooled second moment is exactly one: every token has norm sqrt(d)
+    assert abs((hk ** 2).mean() - 1.0) < 1e-12
+    mu, dv, sk, ku = _moments(hk)
+    assert mu < 0.03 and dv < 0.12 and sk < 0.06 and ku < 0.35, (mu, dv, sk, ku)
+    mu, dv, sk, ku = _moments(hv)
+    assert mu < 0.03 and dv < 0.05 and sk < 0.05 and ku < 0.1, (mu, dv, sk, ku)
+    # the raw keys fail every one of these bounds
+    mu, dv, sk, ku = _moments(np.concatenate([K[s].astype(np.float64) for s in range(16)]))
+    assert mu > 1 and dv > 1 and sk > 0.5 and ku > 1
+
+
+# --- nearest codeword (Methodology §3) --------------------------------------
+
+def test_nearest_codeword_matches_python_brute_force():
+    rng = np.random.default_rng(2)
+    C = rng.standard_normal((16, 4))
+    v = rng.standard_normal((200, 4)) * 1.3
+    got = oracle.nearest_codeword(v, C)
+    for n in range(v.shape[0]):
+        best, bi = None, -1
+        for k in range(C.shape[0]):
+            dist = 0.0
+            for i in range(4):
+                dist += (v[n, i] - C[k, i]) ** 2
+            if best is None or dist < best:
+                best, bi = dist, k
+        assert got[n] == bi
+
+
+def test_product_codebook_reduces_to_scalar_lloyd_max_2bit():
+    """Codebook {+-0.4528, +-1.5104}^4 (the 4-level Lloyd-Max quantizer of
+    N(0,1), Max 1960, applied per coordinate): the nearest codeword is the
+    per-coordinate decision with thresholds 0 and +-0.9816."""
+    levels = np.array([-1.5104, -0.4528, 0.4528, 1.5104])
+    C = np.array(list(itertools.product(levels, repeat=4)))  # index = base-4 digits
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((5000, 4)) * 1.5
+    bins = np.digitize(v, [-0.9816, 0.0, 0.9816])
+    want = ((bins[:, 0] * 4 + bins[:, 1]) * 4 + bins[:, 2]) * 4 + bins[:, 3]
+    assert np.array_equal(oracle.nearest_codeword(v, C), want)
+
+
+def test_product_codebook_reduces_to_sign_bits_1bit():
+    """Codebook {+-sqrt(2/pi)}^8: nearest codeword = the 8 sign bits."""
+    a = np.sqrt(2 / np.pi)
+    C = np.array(list(itertools.product([-a, a], repeat=8)))
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal((3000, 8))
+    bits = (v > 0).astype(np.int64)
+    want = (bits * (1 << np.arange(7, -1, -1))).sum(1)
+    assert np.array_equal(oracle.nearest_codeword(v, C), want)
+
+
+def test_exact_ties_go_to_lowest_index():
+    # binary fractions: the midpoint is exactly equidistant in floating point
+    C = np.array([[0.0, 0, 0, 0], [1.0, 0, 0, 0], [0.0, 0.5, 0, 0]])
+    v = np.array([[0.5, 0, 0, 0], [0.25, 0.25, 0, 0], [1.0, 0.5, 0, 0]])
+    d = oracle.sq_dist_exact(v, C)
+    assert d[0, 0] == d[0, 1] and d[1, 0] == d[1, 2]
+    assert list(oracle.nearest_codeword(v, C)) == [0, 0, 1]
+    C2 = C[[1, 0, 2]]
+    assert list(oracle.nearest_codeword(v, C2)) == [0, 1, 0]
+
+
+# --- scale adjustment (Methodology §3) --------------------------------------
+
+def test_scale_adjust_keeps_parallel_component(cb2):
+    x = _seq(T=256)
+    codes, meta, shift, it = oracle.quantize(x, cb2, 128, return_internals=True)
+    h, hh, a = it["h"], it["h_hat"], it["alpha"]
+    # <alpha h_hat, h> = ||h||^2 = d: the error alpha h_hat - h is orthogonal to h
+    np.testing.assert_allclose(np.sum(a[:, None] * hh * h, axis=1), D, rtol=1e-12)
+    np.testing.assert_allclose(np.sum((a[:, None] * hh - h) * h, axis=1), 0, atol=1e-10)
+    assert np.all(a > 0)
+    # flag off: s2' = s2 exactly
+    _, meta_off, _, it_off = oracle.quantize(x, cb2, 128, scale_adjust_on=False,
+                                             return_internals=True)
+    assert np.array_equal(meta_off[:, 1], it_off["s2"].astype(np.float16))
+    assert np.array_equal(oracle.scale_adjust(np.ones((1, 4)), -np.ones((1, 4))), [1.0])
+
+
+# --- quantize / dequantize --------------------------------------------------
+
+def test_quantize_storage_is_fp16_of_unrounded_values(cb2):
+    x = _seq(T=256)
+    codes, meta, shift, it = oracle.quantize(x, cb2, 128, return_internals=True)
+    assert codes.dtype == np.uint8 and codes.shape == (256, 32)
+    assert np.array_equal(meta[:, 0], it["s1"].astype(np.float16))
+    assert np.array_equal(meta[:, 1], (it["s2"] * it["alpha"]).astype(np.float16))
+    assert np.array_equal(shift, oracle.rotate(it["o"]).astype(np.float16))
+    assert np.array_equal(codes, oracle.nearest_codeword(it["h"].reshape(-1, 4), cb2)
+                          .reshape(256, 32))
+
+
+def test_round_trip_exact_when_vq_is_lossless():
+    """With a codebook that holds every sub-vector of h exactly, alpha = 1 and
+    the (unrounded) byproducts reconstruct x: NSN followed by H is invertible."""
+    G = 2
+    x = _seq(T=2, seed=9)
+    u, s1, o, s2 = oracle.nsn(x, G)
+    h = oracle.rotate(u)
+    C = np.concatenate([h.reshape(-1, 4), np.full((192, 4), 50.0)])  # 64 exact + far fillers
+    codes, _, _, it = oracle.quantize(x, C, G, return_internals=True)
+    np.testing.assert_allclose(it["alpha"], 1.0, rtol=1e-13)
+    meta64 = np.stack([s1, s2], axis=1)
+    xr = oracle.dequantize(codes, meta64, oracle.rotate(o), C, G)
+    np.testing.assert_allclose(xr, x, rtol=1e-12, atol=1e-12)
+
+
+def test_dequantize_equals_channel_domain_formula(cb2):
+    G = 128
+    x = _seq(T=256)
+    codes, meta, shift = oracle.quantize(x, cb2, G)
+    xr = oracle.dequantize(codes, meta, shift, cb2, G)
+    hh = cb2.astype(np.float64)[codes.astype(int)].reshape(256, D)
+    s1 = meta[:, 0:1].astype(np.float64)
+    s2 = meta[:, 1:2].astype(np.float64)
+    o = oracle.rotate(shift.astype(np.float64))  # back to channel domain
+    want = s1 * (s2 * oracle.rotate(hh) + np.repeat(o, G, 0))
+    np.testing.assert_allclose(xr, want, rtol=1e-12, atol=1e-12)
+    # 2-bit reconstruction is a useful approximation of x
+    rel = np.linalg.norm(xr - x) / np.linalg.norm(x)
+    assert rel < 0.35
+
+
+def test_groups_are_independent_flush_equals_one_shot(cb2):
+    """Quantizing group by group (a residual flushed every G tokens) gives the
+    same bytes as one call (summary §4, residual flush)."""
+    G = 128
+    x = _seq(T=512)
+    c, m, s = oracle.quantize(x, cb2, G)
+    for g in range(4):
+        cg, mg, sg = oracle.quantize(x[g * G:(g + 1) * G], cb2, G)
+        assert np.array_equal(cg, c[g * G:(g + 1) * G])
+        assert np.array_equal(mg, m[g * G:(g + 1) * G])
+        assert np.array_equal(sg, s[g:g + 1])
+
+
+def test_zero_group_is_finite_and_reconstructs_zero(cb2):
+    x = np.zeros((128, D))
+    codes, meta, shift = oracle.quantize(x, cb2, 128)
+    assert np.all(meta == 0) and np.all(shift == 0)
+    assert np.all(oracle.dequantize(codes, meta, shift, cb2, 128) == 0)
