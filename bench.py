@@ -1,0 +1,293 @@
+"""Throughput of the NSNQuant hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one pass of the whole per-token path over one batch of synthetic
+input, all through the C ABI of libnsn.so:
+  * prefill quantize: K and V of batch 4 x 32 layers x 8 kv heads, 131072
+    tokens each, head_dim 128, fp16, 2-bit codes (one launch over 2048
+    sequences)                                   -- the dominant kernel
+  * quantized decode attention: batch 16, 32 q heads on 8 kv heads,
+    32768 quantized + 128 fp16 residual tokens (rotating over three cache
+    copies so the 256 MB Infinity Cache cannot hold the working set)
+  * streaming: 128 residual appends of one token per sequence (2048
+    sequences) and the flush of the full residual into the cache
+  * dequantize of the flushed group.
+The codebook (k-means, 20 iterations on 65536 N(0,1) 4-vectors) is built
+once on the GPU before the timed region and reported separately.
+
+Prints ONE JSON line.  ``value`` is the step's algorithmic HBM bytes divided
+by the step time (GB/s); per-kernel rates and the roofline of the dominant
+kernel are attached.  The oracle (numpy float64) is timed on a bounded
+sample of the same workload as ``cpu_baseline``.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+D = 128
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def quant_bytes(n_seq, n_tok, m, G, in_bytes=2):
+    return n_seq * n_tok * (D * in_bytes + D // m + 4) + n_seq * (n_tok // G) * D * 2
+
+
+def attn_bytes(B, Hq, Hkv, Nq, R, m, G):
+    per_tok = 2 * (D // m) + 2 * 4                 # K and V codes + meta
+    shift = 2 * (Nq // G) * D * 2                  # K and V group shifts
+    resid = 2 * R * D * 2
+    return B * Hkv * (Nq * per_tok + shift + resid) + B * Hq * D * (2 + 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=32,
+                    help="layers of the prefill workload (32 = the full workload)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the quantizer shards by sequence with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_calibration_amd as nsnq
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    G, m = 128, 4
+    p = nsnq.Params(sub_dim=m, group_size=G)
+
+    # -- a0: codebook on the GPU (one-time, outside the step)
+    X = torch.from_numpy(synth.codebook_samples(m, 65536, seed=0)).to(dev)
+    cb = torch.empty((256, m), dtype=torch.float32, device=dev)
+    cws = torch.empty(nsnq.nsn_build_codebook_workspace_size(m, 65536), dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    nsnq.nsn_build_codebook(X, cb, cws, iters=20)
+    e1.record()
+    table = torch.empty(nsnq.nsn_table_size(p), dtype=torch.uint8, device=dev)
+    nsnq.nsn_prepare_codebook(p, cb, table)
+    torch.cuda.synchronize()
+    codebook_ms = e0.elapsed_time(e1)
+    log(f"codebook built in {codebook_ms:.1f} ms")
+
+    # -- prefill workload: K and V, batch 4 x layers x 8 heads, 131072 tokens
+    w4 = synth.WORKLOADS["prefill"]
+    L = args.layers
+    per_layer = w4["B"] * w4["Hkv"]
+    n_seq_t = per_layer * L                  # sequences per tensor
+    T = w4["T"]
+    n_seq = 2 * n_seq_t                      # K and V in one launch
+    cap = T + G                              # room for one streamed group
+    x = torch.empty((n_seq, T, D), dtype=torch.float16, device=dev)
+    for layer in range(L):
+        a, b = layer * per_layer, (layer + 1) * per_layer
+        synth.kv_torch(per_layer, T, w4["outlier_scale"], w4["seed"] + layer, dev,
+                       out_k=x[a:b], out_v=x[n_seq_t + a:n_seq_t + b])
+    codes = torch.empty((n_seq, cap, D // m), dtype=torch.uint8, device=dev)
+    meta = torch.empty((n_seq, cap, 2), dtype=torch.float16, device=dev)
+    shift = torch.empty((n_seq, cap // G, D), dtype=torch.float16, device=dev)
+    resid = torch.empty((n_seq, G, D), dtype=torch.float16, device=dev)
+    newtok = torch.randn((G, n_seq, D), dtype=torch.float16, device=dev)
+    deq = torch.empty((n_seq, G, D), dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+    log(f"prefill inputs ready: {n_seq} sequences x {T} tokens ({x.numel() * 2 / 1e9:.1f} GB)")
+
+    # -- decode workload: three independent caches
+    w3 = synth.WORKLOADS["decode"]
+    B3, Hq, Hkv, Nq, R = w3["B"], w3["Hq"], w3["Hkv"], w3["Nq"], w3["R"]
+    scale = 1.0 / math.sqrt(D)
+    caches = []
+    for c in range(3):
+        K3, V3 = synth.kv_torch(B3 * Hkv, Nq + R, w3["outlier_scale"], w3["seed"] + 10 * c, dev)
+        kc = torch.empty((B3, Hkv, Nq, D // m), dtype=torch.uint8, device=dev)
+        km = torch.empty((B3, Hkv, Nq, 2), dtype=torch.float16, device=dev)
+        ks = torch.empty((B3, Hkv, Nq // G, D), dtype=torch.float16, device=dev)
+        vc, vm, vs = torch.empty_like(kc), torch.empty_like(km), torch.empty_like(ks)
+        f = lambda t: t.view(B3 * Hkv, *t.shape[2:])  # noqa: E731
+        nsnq.nsn_quantize(p, K3[:, :Nq], table, f(kc), f(km), f(ks))
+        nsnq.nsn_quantize(p, V3[:, :Nq], table, f(vc), f(vm), f(vs))
+        kr = K3[:, Nq:].contiguous().view(B3, Hkv, R, D)
+        vr = V3[:, Nq:].contiguous().view(B3, Hkv, R, D)
+        q = synth.query_torch((B3, Hq, D), seed=w3["seed"] + 10 * c + 1, device=dev)
+        caches.append(((kc, km, ks), (vc, vm, vs), kr, vr, q))
+        del K3, V3
+    ws_bytes = nsnq.nsn_decode_attention_workspace_size(p, B3, Hq, Hkv, Nq, R, Nq, R, scale)
+    work = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B3, Hq, D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("decode caches ready")
+
+    names = ["quantize", "attention", "append", "flush", "dequantize"]
+    ev = {k: [] for k in names}
+
+    def step(i, record):
+        def timed(name, fn):
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                ev[name].append((a, b))
+            else:
+                fn()
+        timed("quantize", lambda: nsnq.nsn_quantize(p, x, table, codes, meta, shift))
+        kc, vc, kr, vr, q = caches[i % 3]
+        timed("attention", lambda: nsnq.nsn_decode_attention(p, q, kc, vc, kr, vr, table, work, out,
+                                                             Nq, R, scale))
+
+        def appends():
+            for t in range(G):
+                nsnq.nsn_residual_append(newtok[t], resid, t)
+        timed("append", appends)
+        timed("flush", lambda: nsnq.nsn_quantize(p, resid, table, codes[:, T:], meta[:, T:],
+                                                 shift[:, T // G:]))
+        timed("dequantize", lambda: nsnq.nsn_dequantize(p, codes[:, T:], meta[:, T:],
+                                                        shift[:, T // G:], table, deq))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+        log(f"step {i + 1}/{args.steps} issued")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in names}
+    ms_step = wall * 1e3 / args.steps
+
+    qb = quant_bytes(n_seq, T, m, G)
+    ab = attn_bytes(B3, Hq, Hkv, Nq, R, m, G)
+    app_b = G * n_seq * D * 2 * 2
+    fb = quant_bytes(n_seq, G, m, G)
+    db = n_seq * G * (D * 2 + D // m + 4) + n_seq * D * 2
+    step_bytes = qb + ab + app_b + fb + db
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    rates = {
+        "quantize_gbps": qb / (ms["quantize"] * 1e-3) / 1e9,
+        "quantize_fp16_in_gbps": n_seq * T * D * 2 / (ms["quantize"] * 1e-3) / 1e9,
+        "quantize_token_heads_per_s": n_seq * T / (ms["quantize"] * 1e-3),
+        "attention_gbps": ab / (ms["attention"] * 1e-3) / 1e9,
+        "attention_query_tokens_per_s": B3 / (ms["attention"] * 1e-3),
+        "flush_gbps": fb / (ms["flush"] * 1e-3) / 1e9,
+        "dequantize_gbps": db / (ms["dequantize"] * 1e-3) / 1e9,
+    }
+    rates["quantize_frac_hbm"] = rates["quantize_gbps"] / HBM_PEAK_GBPS
+    rates["attention_frac_hbm"] = rates["attention_gbps"] / HBM_PEAK_GBPS
+    log("kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ms.items()))
+    log("rates: " + ", ".join(f"{k} {v:.4g}" for k, v in rates.items()))
+
+    roofline = {
+        "bound": "hbm",
+        "kernel": "quantize_kernel (prefill launch)",
+        "achieved": rates["quantize_gbps"],
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": rates["quantize_gbps"] / HBM_PEAK_GBPS,
+        "traffic": None,
+        "bytes_per_launch": qb,
+        "avg_launch_ms": ms["quantize"],
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, caches[0], G, m, cb.cpu().numpy(), qb, ab, R, Nq, scale, step_bytes)
+
+    line = {
+        "metric": "KV quantize GB/s (fp16 in) + quantized decode-attn GB/s, % of HBM roofline",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"prefill quantize {n_seq_t}x2 seqs x {T} tok fp16 2-bit G={G} "
+                         f"({L} layers x 4 batch x 8 kv heads) + decode attention B={B3} "
+                         f"Hq={Hq} Hkv={Hkv} {Nq}+{R} tok + 128 appends, flush, dequantize"),
+            "head_dim": D, "sub_dim": m, "group_size": G,
+            "step_bytes": step_bytes,
+        },
+        "kernel_ms": ms,
+        "rates": rates,
+        "codebook_build_ms": codebook_ms,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
+    """Time the oracle on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    n_tok = 4096
+    xs = x[:2, :n_tok].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    for s in range(2):
+        oracle.quantize(xs[s], C, G)
+    tq = time.perf_counter() - t0
+    q_rate = quant_bytes(2, n_tok, m, G) / tq            # bytes/s
+    kc, vc, kr, vr, q = cache
+    sl = lambda t: t[0:1, 0:1].cpu().numpy()  # noqa: E731
+    k = tuple(sl(t) for t in kc)
+    v = tuple(sl(t) for t in vc)
+    qn = q[0:1, 0:4].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.decode_attention(qn, k, v, sl(kr), sl(vr), C, G, Nq, R, scale)
+    ta = time.perf_counter() - t0
+    a_rate = (Nq * (2 * (128 // m) + 8) + 2 * (Nq // G) * 256 + 2 * R * 256) / ta
+    step_s = qb / q_rate + ab / a_rate
+    log(f"cpu oracle: quantize {q_rate / 1e9:.4f} GB/s ({tq:.1f}s), attention "
+        f"{a_rate / 1e9:.4f} GB/s ({ta:.1f}s)")
+    return {
+        "value": step_bytes / step_s / 1e9,
+        "unit": "GB/s",
+        "cores": cores,
+        "blas_threads": blas_threads,
+        "kind": "oracle",
+        "sample": (f"oracle.quantize on 2 prefill sequences x {n_tok} tokens ({tq:.1f} s) and "
+                   f"oracle.decode_attention on one (batch, kv head) of the decode cache with its "
+                   f"4 q heads ({ta:.1f} s); step time extrapolated from the two rates"),
+        "quantize_gbps": q_rate / 1e9,
+        "attention_gbps": a_rate / 1e9,
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * nsn.h -- C ABI of the NSNQuant KV-cache quantization library (gfx950).
+ *
+ * The method: each KV token of one head (d = 128 channels) is normalized to
+ * norm sqrt(d) (scale s1), centred by the per-channel mean of its token
+ * group (o), normalized again (s2), rotated by the orthonormal Hadamard
+ * transform, and every m-dimensional sub-vector (m = 4: 2 bits per value,
+ * m = 8: 1 bit) is replaced by the index of its nearest codeword in one
+ * 256-entry codebook built by k-means on standard-normal samples.
+ * [NSNQuant technical summary (gist.science, es/de), Methodology §1 NSN,
+ *  §2 Hadamard transform, §3 vector quantization and codebook,
+ *  §4 implementation details; authors' README (DHdroid/NSNQuant), Overview.]
+ *
+ * Conventions for every call
+ *  - Pointers documented "device" are HIP device memory owned by the caller;
+ *    the library never allocates, frees or retains them.  Every device
+ *    pointer must be 16-byte aligned.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronize.  Kernel faults surface at the caller's
+ *    next synchronization.
+ *  - All arguments are validated before any HIP call.  Invalid values
+ *    return NSN_ERR_INVALID_ARG, supported-but-unimplemented shapes
+ *    NSN_ERR_UNSUPPORTED, a too-small workspace NSN_ERR_WORKSPACE; a failed
+ *    launch returns NSN_ERR_HIP.  A detail string for the most recent error
+ *    on the calling thread is available from nsn_last_error().
+ *  - Inputs must be finite.  Non-finite inputs give unspecified output but
+ *    never an out-of-bounds access.
+ *  - The library keeps no mutable global state besides the thread-local
+ *    error string; calls on different streams may run concurrently as long
+ *    as their output buffers do not overlap.
+ */
+#ifndef NSN_H
+#define NSN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NSN_OK = 0,
+  NSN_ERR_INVALID_ARG = 1,
+  NSN_ERR_UNSUPPORTED = 2,
+  NSN_ERR_WORKSPACE = 3,
+  NSN_ERR_HIP = 4
+} nsn_status;
+
+typedef enum { NSN_F16 = 0, NSN_F32 = 1 } nsn_dtype;
+
+/* nsn_params.flags: per-token scale adjustment (NSNQuant summary, §3:
+ * the quantized vector is rescaled so that its component along the
+ * original vector is preserved; folded into the stored s2). */
+#define NSN_SCALE_ADJUST 1u
+
+typedef struct {
+  int32_t head_dim;   /* d: must be 128 */
+  int32_t sub_dim;    /* m: 4 (2-bit codes) or 8 (1-bit codes) */
+  int32_t n_codes;    /* K: must be 256 (one byte per code) */
+  int32_t group_size; /* G: tokens per Shift group; 128 or 256 */
+  uint32_t flags;     /* NSN_SCALE_ADJUST or 0 */
+} nsn_params;
+
+/* Size in bytes of a prepared codebook for these params (codebook, squared
+ * norms and search tables); constant for the supported shapes. */
+size_t nsn_table_size(const nsn_params* p);
+
+/*
+ * nsn_build_codebook -- Lloyd k-means codebook on standard-normal samples.
+ * [NSNQuant summary §3, codebook construction: k-means over synthetic
+ *  N(0,1) data, no calibration set; README, Overview.]
+ *
+ * samples   device, float64 [n_samples][sub_dim], row-major; the random
+ *           N(0,1) draw is the caller's (any generator).
+ * codebook  device, float32 [n_codes][sub_dim], written.
+ * Steps: init = the first n_codes samples; `iters` times: assign every
+ * sample to its nearest centroid (exact squared distance in float64, lowest
+ * index on ties), then set each centroid to the mean of its members summed
+ * in sample order (a centroid with no members keeps its value).  The final
+ * centroids are rounded to the nearest fp16 value (ties to even) and stored
+ * as float32.  Deterministic.
+ * workspace device, >= nsn_build_codebook_workspace_size() bytes.
+ * Requires n_codes == 256, sub_dim in {4, 8}, n_codes <= n_samples
+ * <= 2^26, 1 <= iters <= 1000.
+ */
+size_t nsn_build_codebook_workspace_size(int32_t sub_dim, int32_t n_codes,
+                                         int64_t n_samples);
+nsn_status nsn_build_codebook(int32_t sub_dim, int32_t n_codes,
+                              int64_t n_samples, int32_t iters,
+                              const double* samples, float* codebook,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * nsn_prepare_codebook -- derive the device search tables from a codebook.
+ * codebook  device, float32 [256][sub_dim] (entries must be finite).
+ * table     device, nsn_table_size(p) bytes, written; passed to every
+ *           quantize / dequantize / attention call using this codebook.
+ */
+nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook,
+                                void* table, size_t table_bytes,
+                                void* stream);
+
+/*
+ * nsn_quantize -- compress whole token groups.
+ * [NSNQuant summary §1 (Normalize, Shift over the group, Normalize),
+ *  §2 (Hadamard rotation), §3 (nearest codeword, scale adjustment),
+ *  §4 (a full residual is quantized and appended).]
+ *
+ * x       device, [n_seq][n_tok][128] of in_dtype (fp16 or fp32); tokens of
+ *         one sequence are contiguous (row stride 128 elements), sequences
+ *         `x_seq_stride` elements apart.  A "sequence" is one (batch, layer,
+ *         head) of K or of V; any leading dims are flattened into n_seq.
+ * n_tok   multiple of group_size (only whole groups are quantized); 0 is a
+ *         no-op.
+ * Outputs (device; token t of sequence s):
+ *   codes  uint8 at codes + s*codes_seq_stride + t*(128/m) + j, j < 128/m:
+ *          the code of sub-vector j = rotated channels [m*j, m*j+m).
+ *   meta   fp16 pair at meta + s*meta_seq_stride + 2*t: (s1, s2'), where
+ *          s1 = ||x_t||/sqrt(128) and s2' = s2 * alpha (alpha = 1 without
+ *          NSN_SCALE_ADJUST).
+ *   shift  fp16 [128] at shift + s*shift_seq_stride + (t/G)*128: the group's
+ *          channel mean o, stored rotated (H o / sqrt(128)).
+ * Strides let a flush write into a preallocated cache at a group offset:
+ * pass pointers advanced to the offset and the cache's sequence strides.
+ */
+nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype,
+                        const void* x, int64_t n_seq, int64_t n_tok,
+                        int64_t x_seq_stride, const void* table,
+                        uint8_t* codes, int64_t codes_seq_stride,
+                        uint16_t* meta, int64_t meta_seq_stride,
+                        uint16_t* shift, int64_t shift_seq_stride,
+                        void* stream);
+
+/*
+ * nsn_dequantize -- reconstruct tokens from codes and stored byproducts.
+ * [NSNQuant summary §1 (the byproducts reconstruct the tensor), §4
+ *  (dequantization kernels).]
+ * x_hat_t = (H/sqrt(128)) [ s1 (s2' c(codes_t) + o'_g) ], the stored fp16
+ * values taken as exact.  Layouts as nsn_quantize; output x_hat
+ * [n_seq][n_tok][128] of out_dtype, sequences out_seq_stride elements apart.
+ * n_tok must be a multiple of group_size.
+ */
+nsn_status nsn_dequantize(const nsn_params* p, const uint8_t* codes,
+                          int64_t codes_seq_stride, const uint16_t* meta,
+                          int64_t meta_seq_stride, const uint16_t* shift,
+                          int64_t shift_seq_stride, const void* table,
+                          int64_t n_seq, int64_t n_tok, nsn_dtype out_dtype,
+                          void* x_hat, int64_t out_seq_stride, void* stream);
+
+/*
+ * nsn_residual_append -- write one new fp16 token per sequence into the
+ * full-precision residual window at position `pos`.
+ * [NSNQuant summary §4: recent tokens stay in full precision until the
+ *  residual is full, then it is quantized and appended to the cache.]
+ * tok    device fp16 [n_seq][128] (contiguous).
+ * resid  device fp16, token t of sequence s at resid + s*resid_seq_stride
+ *        + t*128; requires 0 <= pos < resid_capacity.
+ */
+nsn_status nsn_residual_append(const uint16_t* tok, int64_t n_seq,
+                               uint16_t* resid, int64_t resid_seq_stride,
+                               int64_t resid_capacity, int64_t pos,
+                               void* stream);
+
+typedef struct {
+  int32_t batch;          /* B */
+  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;     /* Hkv; q head h reads kv head h / (Hq/Hkv) */
+  int32_t n_quant_tok;    /* quantized tokens per (b, kv head); multiple of G */
+  int32_t n_resid_tok;    /* valid fp16 residual tokens, 0..resid_capacity */
+  int64_t cache_capacity; /* token slots per (b, kv head) in the code/meta
+                             arrays; multiple of G, >= n_quant_tok */
+  int64_t resid_capacity; /* token slots per (b, kv head) in the residual */
+  float softmax_scale;    /* e.g. 1/sqrt(128) */
+} nsn_attn_shape;
+
+/*
+ * nsn_decode_attention -- one query token per (batch, q head) attends over
+ * its kv head's quantized cache plus the fp16 residual window.
+ * [NSNQuant summary §4: quantized part plus full-precision residual; the
+ *  score uses the NSN byproducts s1, s2, o directly.]
+ *
+ * With q' = H q / sqrt(128), on quantized token t of group g:
+ *   score_t = scale * s1_t * (s2'_t <q', c(codes_t)> + <q', o'_g>)
+ * and on residual token r: score_r = scale * <q, k_r>.  Softmax over all
+ * n_quant_tok + n_resid_tok scores (float32, max-subtracted); values are
+ * the dequantized V tokens and the residual V tokens.  No mask, no RoPE.
+ *
+ * q        device fp16 [B][Hq][128].
+ * k_codes, v_codes   device uint8 [B][Hkv][cache_capacity][128/m].
+ * k_meta,  v_meta    device fp16  [B][Hkv][cache_capacity][2].
+ * k_shift, v_shift   device fp16  [B][Hkv][cache_capacity/G][128].
+ * k_resid, v_resid   device fp16  [B][Hkv][resid_capacity][128].
+ * workspace          device, >= nsn_decode_attention_workspace_size().
+ * out      device fp32 [B][Hq][128].
+ * Requires n_quant_tok + n_resid_tok >= 1.
+ */
+size_t nsn_decode_attention_workspace_size(const nsn_params* p,
+                                           const nsn_attn_shape* s);
+nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s,
+                                const uint16_t* q, const uint8_t* k_codes,
+                                const uint16_t* k_meta, const uint16_t* k_shift,
+                                const uint8_t* v_codes, const uint16_t* v_meta,
+                                const uint16_t* v_shift, const uint16_t* k_resid,
+                                const uint16_t* v_resid, const void* table,
+                                void* workspace, size_t workspace_bytes,
+                                float* out, void* stream);
+
+/* Static description of a status code. */
+const char* nsn_status_string(nsn_status s);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* nsn_last_error(void);
+/* Library version string. */
+const char* nsn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NSN_H */

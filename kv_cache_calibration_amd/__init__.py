@@ -1,0 +1,195 @@
+"""NSNQuant KV-cache quantization for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libnsn.so`` (include/nsn.h): every
+function here only marshals torch device tensors into pointers, sizes and
+strides and calls the function of the same name; all computation runs in the
+library's HIP kernels on the caller's current HIP stream.
+
+Tensor conventions (dim 0 is always the flattened sequence axis; inner dims
+must be contiguous):
+    x       (n_seq, n_tok, 128)            fp16 or fp32
+    codes   (n_seq, cap, 128 // m)         uint8
+    meta    (n_seq, cap, 2)                fp16   (s1, s2')
+    shift   (n_seq, cap // G, 128)         fp16   rotated group mean
+    table   (nsn_table_size,)              uint8  prepared codebook
+"""
+
+import ctypes
+
+from . import _lib
+from ._lib import NSN_SCALE_ADJUST, NsnError  # noqa: F401
+
+__all__ = [
+    "Params",
+    "NsnError",
+    "nsn_table_size",
+    "nsn_build_codebook",
+    "nsn_prepare_codebook",
+    "nsn_quantize",
+    "nsn_dequantize",
+    "nsn_residual_append",
+    "nsn_decode_attention",
+    "nsn_decode_attention_workspace_size",
+    "lib_path",
+]
+
+
+def lib_path():
+    return _lib.LIB_PATH
+
+
+class Params:
+    """Python view of ``nsn_params``."""
+
+    def __init__(self, sub_dim=4, group_size=128, scale_adjust=True, head_dim=128, n_codes=256):
+        self.c = _lib.nsn_params(head_dim, sub_dim, n_codes, group_size,
+                                 NSN_SCALE_ADJUST if scale_adjust else 0)
+
+    @property
+    def sub_dim(self):
+        return self.c.sub_dim
+
+    @property
+    def group_size(self):
+        return self.c.group_size
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be HIP device tensors")
+
+
+def _inner_contig(t, inner):
+    """dims >= 1 contiguous with the given inner sizes."""
+    if tuple(t.shape[1:]) != tuple(inner) and inner is not None:
+        raise ValueError(f"expected inner shape {inner}, got {tuple(t.shape[1:])}")
+    st = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if t.shape[d] > 1 and t.stride(d) != st:
+            raise ValueError("inner dimensions must be contiguous")
+        st *= t.shape[d]
+
+
+def nsn_table_size(params):
+    return int(_lib.load().nsn_table_size(ctypes.byref(params.c)))
+
+
+def nsn_build_codebook(samples, codebook, workspace, iters=20, n_codes=256, stream=None):
+    """samples float64 (n, m) device; codebook float32 (n_codes, m) device (written)."""
+    import torch
+    _dev(samples, codebook, workspace)
+    if samples.dtype != torch.float64 or codebook.dtype != torch.float32:
+        raise ValueError("samples must be float64 and codebook float32")
+    if not samples.is_contiguous() or not codebook.is_contiguous():
+        raise ValueError("samples and codebook must be contiguous")
+    lib = _lib.load()
+    _lib.check(lib.nsn_build_codebook(samples.shape[1], n_codes, samples.shape[0], iters,
+                                      _ptr(samples), _ptr(codebook), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+
+
+def nsn_build_codebook_workspace_size(sub_dim, n_samples, n_codes=256):
+    return int(_lib.load().nsn_build_codebook_workspace_size(sub_dim, n_codes, n_samples))
+
+
+def nsn_prepare_codebook(params, codebook, table, stream=None):
+    _dev(codebook, table)
+    _lib.check(_lib.load().nsn_prepare_codebook(ctypes.byref(params.c), _ptr(codebook),
+                                                _ptr(table), table.numel() * table.element_size(),
+                                                _stream(stream)))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return _lib.NSN_F16
+    if t.dtype == torch.float32:
+        return _lib.NSN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def nsn_quantize(params, x, table, codes, meta, shift, n_tok=None, stream=None):
+    """Quantize x (n_seq, n_tok, 128) into codes/meta/shift (see module doc).
+
+    The output tensors may be views into a larger cache (e.g. advanced to a
+    group offset); their dim-0 strides are passed through."""
+    _dev(x, table, codes, meta, shift)
+    n_tok = x.shape[1] if n_tok is None else n_tok
+    _inner_contig(x, (x.shape[1], 128))
+    _inner_contig(codes, None)
+    _inner_contig(meta, None)
+    _inner_contig(shift, None)
+    lib = _lib.load()
+    _lib.check(lib.nsn_quantize(ctypes.byref(params.c), _dtype_code(x), _ptr(x), x.shape[0], n_tok,
+                                x.stride(0), _ptr(table), _ptr(codes), codes.stride(0), _ptr(meta),
+                                meta.stride(0), _ptr(shift), shift.stride(0), _stream(stream)))
+
+
+def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=None):
+    _dev(codes, meta, shift, table, out)
+    n_tok = out.shape[1] if n_tok is None else n_tok
+    _inner_contig(out, (out.shape[1], 128))
+    lib = _lib.load()
+    _lib.check(lib.nsn_dequantize(ctypes.byref(params.c), _ptr(codes), codes.stride(0), _ptr(meta),
+                                  meta.stride(0), _ptr(shift), shift.stride(0), _ptr(table),
+                                  out.shape[0], n_tok, _dtype_code(out), _ptr(out), out.stride(0),
+                                  _stream(stream)))
+
+
+def nsn_residual_append(tok, resid, pos, stream=None):
+    """tok fp16 (n_seq, 128); resid fp16 (n_seq, cap, 128)."""
+    _dev(tok, resid)
+    if not tok.is_contiguous():
+        raise ValueError("tok must be contiguous")
+    _inner_contig(resid, (resid.shape[1], 128))
+    lib = _lib.load()
+    _lib.check(lib.nsn_residual_append(_ptr(tok), tok.shape[0], _ptr(resid), resid.stride(0),
+                                       resid.shape[1], pos, _stream(stream)))
+
+
+def _shape(batch, n_q_heads, n_kv_heads, n_quant_tok, n_resid_tok, cache_capacity,
+           resid_capacity, softmax_scale):
+    return _lib.nsn_attn_shape(batch, n_q_heads, n_kv_heads, n_quant_tok, n_resid_tok,
+                               cache_capacity, resid_capacity, softmax_scale)
+
+
+def nsn_decode_attention_workspace_size(params, batch, n_q_heads, n_kv_heads, n_quant_tok,
+                                        n_resid_tok, cache_capacity, resid_capacity,
+                                        softmax_scale):
+    s = _shape(batch, n_q_heads, n_kv_heads, n_quant_tok, n_resid_tok, cache_capacity,
+               resid_capacity, softmax_scale)
+    return int(_lib.load().nsn_decode_attention_workspace_size(ctypes.byref(params.c),
+                                                               ctypes.byref(s)))
+
+
+def nsn_decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
+                         n_quant_tok, n_resid_tok, softmax_scale, stream=None):
+    """q fp16 (B, Hq, 128); k_cache/v_cache = (codes (B, Hkv, cap, 128/m) uint8,
+    meta (B, Hkv, cap, 2) fp16, shift (B, Hkv, cap/G, 128) fp16), all contiguous;
+    k_resid/v_resid fp16 (B, Hkv, Rcap, 128) contiguous; out fp32 (B, Hq, 128)."""
+    kc, km, ks = k_cache
+    vc, vm, vs = v_cache
+    _dev(q, kc, km, ks, vc, vm, vs, k_resid, v_resid, table, workspace, out)
+    for t in (q, kc, km, ks, vc, vm, vs, k_resid, v_resid, out):
+        if not t.is_contiguous():
+            raise ValueError("attention tensors must be contiguous")
+    B, Hq, _ = q.shape
+    Hkv, cap = kc.shape[1], kc.shape[2]
+    s = _shape(B, Hq, Hkv, n_quant_tok, n_resid_tok, cap, k_resid.shape[2], softmax_scale)
+    lib = _lib.load()
+    _lib.check(lib.nsn_decode_attention(
+        ctypes.byref(params.c), ctypes.byref(s), _ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc),
+        _ptr(vm), _ptr(vs), _ptr(k_resid), _ptr(v_resid), _ptr(table), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))

@@ -1,0 +1,164 @@
+// Codebook kernels: Lloyd k-means on standard-normal samples, fp16 rounding,
+// and the prepared-codebook table.
+// [NSNQuant summary (gist.science), Methodology §3, codebook construction:
+//  one global codebook from k-means over synthetic N(0,1) data; authors'
+//  README, Overview.]
+//
+// Everything here is float64 with contraction disabled, so distances are
+// the exact-form sum of rounded squares and each centroid is the sequential
+// sum of its members in sample order divided by the member count.  The
+// result is deterministic and reproducible bit for bit.
+#include "nsn_device.h"
+#include "nsn_launch.h"
+
+namespace nsn {
+
+namespace {
+
+constexpr int kAssignThreads = 256;
+
+// Label every sample with its nearest centroid (lowest index on ties).
+template <int M>
+__global__ __launch_bounds__(kAssignThreads) void kmeans_assign(
+    const double* __restrict__ x, int64_t n, const double* __restrict__ cent,
+    int32_t* __restrict__ labels) {
+#pragma clang fp contract(off)
+  __shared__ double c[kCodes * M];
+  for (int i = threadIdx.x; i < kCodes * M; i += kAssignThreads) c[i] = cent[i];
+  __syncthreads();
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * kAssignThreads + threadIdx.x;
+  if (s >= n) return;
+  double v[M];
+#pragma unroll
+  for (int e = 0; e < M; ++e) v[e] = x[s * M + e];
+  double best = 0.0;
+  int bi = 0;
+  for (int k = 0; k < kCodes; ++k) {
+    double d = 0.0;
+#pragma unroll
+    for (int e = 0; e < M; ++e) {
+      const double t = v[e] - c[k * M + e];
+      const double sq = t * t;
+      d = (e == 0) ? sq : d + sq;
+    }
+    if (k == 0 || d < best) {
+      best = d;
+      bi = k;
+    }
+  }
+  labels[s] = bi;
+}
+
+// New centroid (k, e) = sequential sum over samples with label k, in sample
+// order, divided by the count; an empty cluster keeps its centroid.
+template <int M>
+__global__ __launch_bounds__(256) void kmeans_update(const double* __restrict__ x, int64_t n,
+                                                     const int32_t* __restrict__ labels,
+                                                     double* __restrict__ cent) {
+#pragma clang fp contract(off)
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id >= kCodes * M) return;
+  const int k = id / M, e = id % M;
+  double s = 0.0;
+  int64_t cnt = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (labels[i] == k) {
+      s = s + x[i * M + e];
+      ++cnt;
+    }
+  }
+  if (cnt > 0) cent[id] = s / static_cast<double>(cnt);
+}
+
+template <int M>
+__global__ void kmeans_init(const double* __restrict__ x, double* __restrict__ cent) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id < kCodes * M) cent[id] = x[id];
+}
+
+// Round a double to the nearest fp16 value (ties to even), returned exactly
+// as a float.  Normal fp16 range: 11 significant bits; below 2^-14 the
+// spacing is 2^-24; beyond 65504 (after rounding) the result is infinite.
+__device__ float round_to_half(double v) {
+  if (!(v == v)) return __builtin_nanf("");
+  const double a = fabs(v);
+  double r;
+  if (a < 6.103515625e-05) {  // 2^-14: subnormal spacing 2^-24
+    r = rint(v * 16777216.0) / 16777216.0;
+  } else {
+    const int e = ilogb(a);                 // 2^e <= a < 2^(e+1)
+    const double q = ldexp(1.0, e - 10);    // spacing of fp16 at this binade
+    r = rint(v / q) * q;
+  }
+  if (fabs(r) > 65504.0) r = v > 0 ? __builtin_huge_val() : -__builtin_huge_val();
+  return static_cast<float>(r);
+}
+
+template <int M>
+__global__ void kmeans_finish(const double* __restrict__ cent, float* __restrict__ out) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id < kCodes * M) out[id] = round_to_half(cent[id]);
+}
+
+template <int M>
+__global__ void prepare_kernel(const float* __restrict__ cb, uint8_t* __restrict__ table) {
+  const int k = threadIdx.x;  // 256 threads, one per codeword
+  float* tc = reinterpret_cast<float*>(table + kTabCodebook);
+  float* tn = reinterpret_cast<float*>(table + kTabNorm2);
+  uint16_t* th = reinterpret_cast<uint16_t*>(table + kTabCodebookH);
+  float n2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < M; ++e) {
+    const float c = cb[k * M + e];
+    tc[k * M + e] = c;
+    th[k * M + e] = f2h(c);
+    n2 = fmaf(c, c, n2);
+  }
+  tn[k] = n2;
+}
+
+template <int M>
+hipError_t build(int64_t n, int iters, const double* samples, float* codebook, void* ws,
+                 hipStream_t s) {
+  int32_t* labels = static_cast<int32_t*>(ws);
+  const size_t lab_bytes = (static_cast<size_t>(n) * 4 + 255) & ~static_cast<size_t>(255);
+  double* cent = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + lab_bytes);
+  const int cb_blocks = (kCodes * M + 255) / 256;
+  hipLaunchKernelGGL(kmeans_init<M>, dim3(cb_blocks), dim3(256), 0, s, samples, cent);
+  const unsigned ab = static_cast<unsigned>((n + kAssignThreads - 1) / kAssignThreads);
+  for (int it = 0; it < iters; ++it) {
+    hipLaunchKernelGGL(kmeans_assign<M>, dim3(ab), dim3(kAssignThreads), 0, s, samples, n, cent,
+                       labels);
+    hipLaunchKernelGGL(kmeans_update<M>, dim3(cb_blocks), dim3(256), 0, s, samples, n, labels,
+                       cent);
+  }
+  hipLaunchKernelGGL(kmeans_finish<M>, dim3(cb_blocks), dim3(256), 0, s, cent, codebook);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t build_codebook_workspace(int sub_dim, int n_codes, int64_t n) {
+  const size_t lab_bytes = (static_cast<size_t>(n) * 4 + 255) & ~static_cast<size_t>(255);
+  return lab_bytes + static_cast<size_t>(n_codes) * sub_dim * sizeof(double);
+}
+
+hipError_t launch_build_codebook(int sub_dim, int n_codes, int64_t n, int iters,
+                                 const double* samples, float* codebook, void* ws,
+                                 hipStream_t s) {
+  (void)n_codes;
+  return sub_dim == 4 ? build<4>(n, iters, samples, codebook, ws, s)
+                      : build<8>(n, iters, samples, codebook, ws, s);
+}
+
+hipError_t launch_prepare_codebook(const float* codebook, int sub_dim, void* table,
+                                   hipStream_t s) {
+  uint8_t* t = static_cast<uint8_t*>(table);
+  if (sub_dim == 4)
+    hipLaunchKernelGGL(prepare_kernel<4>, dim3(1), dim3(256), 0, s, codebook, t);
+  else
+    hipLaunchKernelGGL(prepare_kernel<8>, dim3(1), dim3(256), 0, s, codebook, t);
+  return hipGetLastError();
+}
+
+}  // namespace nsn

@@ -1,0 +1,77 @@
+// Device helpers shared by the NSNQuant HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace nsn {
+
+constexpr int kD = 128;      // head_dim
+constexpr int kCodes = 256;  // codebook entries
+constexpr int kWave = 64;
+
+// Prepared-codebook blob layout (bytes).  Written by nsn_prepare_codebook.
+//   [0, 8192)        float32 codebook [256][m], m in {4, 8}
+//   [8192, 9216)     float32 squared norms [256]
+//   [9216, 13312)    fp16 codebook [256][m] (exact: entries are fp16 values
+//                    when built by nsn_build_codebook; otherwise rounded)
+constexpr size_t kTabCodebook = 0;
+constexpr size_t kTabNorm2 = 8192;
+constexpr size_t kTabCodebookH = 9216;
+constexpr size_t kTabBytes = 16384;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte load: data read once should not evict
+// reused lines from L2/MALL.
+__device__ __forceinline__ u32x4 load_nt16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+__device__ __forceinline__ uint16_t f2h(float f) {
+  // round to nearest even (v_cvt_f16_f32 in the default mode)
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<__half>(__half v) {
+  return __half2float(v);
+}
+
+// In-register unnormalized Walsh-Hadamard transform of N values in Sylvester
+// (natural) order: v <- H_N v.  Every index is a compile-time constant once
+// the loops are unrolled, so the array stays in VGPRs.
+template <int N>
+__device__ __forceinline__ void fwht_regs(float (&v)[N]) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i];
+        const float b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+}  // namespace nsn

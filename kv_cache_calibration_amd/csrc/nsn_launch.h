@@ -1,0 +1,75 @@
+// Host-side launchers of the NSNQuant kernels.  Arguments are validated by
+// the C ABI layer (nsn_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nsn {
+
+struct QuantArgs {
+  const void* x;
+  int in_f32;
+  int64_t n_seq, n_tok, x_seq_stride;
+  const void* table;
+  uint8_t* codes;
+  int64_t codes_seq_stride;
+  uint16_t* meta;
+  int64_t meta_seq_stride;
+  uint16_t* shift;
+  int64_t shift_seq_stride;
+  int sub_dim, group_size, scale_adjust;
+};
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+struct DequantArgs {
+  const uint8_t* codes;
+  int64_t codes_seq_stride;
+  const uint16_t* meta;
+  int64_t meta_seq_stride;
+  const uint16_t* shift;
+  int64_t shift_seq_stride;
+  const void* table;
+  int64_t n_seq, n_tok;
+  int out_f32;
+  void* out;
+  int64_t out_seq_stride;
+  int sub_dim, group_size;
+};
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
+
+hipError_t launch_prepare_codebook(const float* codebook, int sub_dim,
+                                   void* table, hipStream_t s);
+
+hipError_t launch_build_codebook(int sub_dim, int n_codes, int64_t n,
+                                 int iters, const double* samples,
+                                 float* codebook, void* workspace,
+                                 hipStream_t s);
+size_t build_codebook_workspace(int sub_dim, int n_codes, int64_t n);
+
+hipError_t launch_residual_append(const uint16_t* tok, int64_t n_seq,
+                                  uint16_t* resid, int64_t resid_seq_stride,
+                                  int64_t pos, hipStream_t s);
+
+struct AttnArgs {
+  int B, Hq, Hkv, n_quant, n_resid;
+  int64_t cap, rcap;
+  float scale;
+  int sub_dim, group_size;
+  const uint16_t* q;
+  const uint8_t *kc, *vc;
+  const uint16_t *km, *vm, *ks, *vs, *kr, *vr;
+  const void* table;
+  float* work;
+  float* out;
+  int n_split;   // chunks per (b, kv-head block)
+  int chunk;     // quantized tokens per chunk (multiple of group_size)
+};
+// Split choice shared by the workspace-size query and the launch.
+void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size,
+               int* n_split, int* chunk);
+size_t attn_workspace_bytes(int B, int Hq, int n_split);
+hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace nsn

@@ -1,0 +1,170 @@
+"""The C-ABI library loads, exports every function include/nsn.h declares, and
+rejects invalid arguments before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_calibration_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsn.h")
+
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10004)
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def P(sub_dim=4, G=128, flags=1, d=128, K=256):
+    return ctypes.byref(_lib.nsn_params(d, sub_dim, K, G, flags))
+
+
+def test_header_declares_the_four_method_calls():
+    names = declared_functions()
+    for n in ("nsn_build_codebook", "nsn_quantize", "nsn_dequantize", "nsn_decode_attention"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.nsn_version().decode().startswith("nsnq")
+    for s in range(5):
+        assert lib.nsn_status_string(s)
+    assert lib.nsn_status_string(99) == b"unknown status"
+
+
+def _q(lib, params, n_seq=2, n_tok=256, x=FAKE, codes=FAKE, meta=FAKE, shift=FAKE,
+       xs=None, cs=None, ms=None, ss=None, dtype=0, table=FAKE):
+    nsub = 32
+    xs = n_tok * 128 if xs is None else xs
+    cs = n_tok * nsub if cs is None else cs
+    ms = n_tok * 2 if ms is None else ms
+    ss = (n_tok // 128) * 128 if ss is None else ss
+    return lib.nsn_quantize(params, dtype, x, n_seq, n_tok, xs, table, codes, cs, meta, ms,
+                            shift, ss, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(params=None), _lib.NSN_ERR_INVALID_ARG),
+    (dict(params=P(d=64)), _lib.NSN_ERR_UNSUPPORTED),
+    (dict(params=P(sub_dim=2)), _lib.NSN_ERR_UNSUPPORTED),
+    (dict(params=P(K=512)), _lib.NSN_ERR_UNSUPPORTED),
+    (dict(params=P(G=64)), _lib.NSN_ERR_UNSUPPORTED),
+    (dict(params=P(flags=8)), _lib.NSN_ERR_INVALID_ARG),
+    (dict(n_tok=200), _lib.NSN_ERR_INVALID_ARG),
+    (dict(n_tok=-128), _lib.NSN_ERR_INVALID_ARG),
+    (dict(x=NULL), _lib.NSN_ERR_INVALID_ARG),
+    (dict(table=NULL), _lib.NSN_ERR_INVALID_ARG),
+    (dict(codes=MISALIGNED), _lib.NSN_ERR_INVALID_ARG),
+    (dict(xs=100), _lib.NSN_ERR_INVALID_ARG),
+    (dict(cs=8), _lib.NSN_ERR_INVALID_ARG),
+    (dict(ms=3), _lib.NSN_ERR_INVALID_ARG),
+    (dict(ss=7), _lib.NSN_ERR_INVALID_ARG),
+    (dict(dtype=7), _lib.NSN_ERR_INVALID_ARG),
+])
+def test_quantize_validation(lib, kw, status):
+    params = kw.pop("params", P())
+    st = _q(lib, params, **kw)
+    assert st == status
+    assert lib.nsn_last_error()
+
+
+def test_quantize_empty_is_ok_without_touching_pointers(lib):
+    assert _q(lib, P(), n_seq=0, x=NULL, codes=NULL, meta=NULL, shift=NULL) == _lib.NSN_OK
+    assert _q(lib, P(), n_tok=0, x=NULL, codes=NULL, meta=NULL, shift=NULL) == _lib.NSN_OK
+
+
+def test_dequantize_validation(lib):
+    f = lib.nsn_dequantize
+    ok_args = dict(codes=FAKE, cs=256 * 32, meta=FAKE, ms=512, shift=FAKE, ss=256, table=FAKE,
+                   n_seq=2, n_tok=256, dt=0, out=FAKE, os_=256 * 128)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return f(P(), a["codes"], a["cs"], a["meta"], a["ms"], a["shift"], a["ss"], a["table"],
+                 a["n_seq"], a["n_tok"], a["dt"], a["out"], a["os_"], NULL)
+    assert call(n_tok=100) == _lib.NSN_ERR_INVALID_ARG
+    assert call(out=NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert call(dt=5) == _lib.NSN_ERR_INVALID_ARG
+    assert call(os_=64) == _lib.NSN_ERR_INVALID_ARG
+    assert call(meta=MISALIGNED) == _lib.NSN_ERR_INVALID_ARG
+    assert call(n_seq=0, codes=NULL) == _lib.NSN_OK
+
+
+def test_build_codebook_validation(lib):
+    f = lib.nsn_build_codebook
+    ws = lib.nsn_build_codebook_workspace_size(4, 256, 65536)
+    assert ws >= 65536 * 4 + 256 * 4 * 8
+    assert f(3, 256, 65536, 20, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_UNSUPPORTED
+    assert f(4, 128, 65536, 20, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_UNSUPPORTED
+    assert f(4, 256, 100, 20, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, 65536, 0, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, 65536, 20, NULL, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, 65536, 20, FAKE, FAKE, FAKE, ws - 1, NULL) == _lib.NSN_ERR_WORKSPACE
+
+
+def test_prepare_and_append_validation(lib):
+    ts = lib.nsn_table_size(P())
+    assert ts >= 256 * 8 * 4
+    assert lib.nsn_prepare_codebook(P(), FAKE, FAKE, ts - 1, NULL) == _lib.NSN_ERR_WORKSPACE
+    assert lib.nsn_prepare_codebook(P(), NULL, FAKE, ts, NULL) == _lib.NSN_ERR_INVALID_ARG
+    a = lib.nsn_residual_append
+    assert a(FAKE, 4, FAKE, 128 * 128, 128, 128, NULL) == _lib.NSN_ERR_INVALID_ARG  # pos == cap
+    assert a(FAKE, 4, FAKE, 128 * 128, 128, -1, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert a(FAKE, 4, FAKE, 100, 128, 3, NULL) == _lib.NSN_ERR_INVALID_ARG  # stride too small
+    assert a(NULL, 0, NULL, 0, 128, 3, NULL) == _lib.NSN_OK
+
+
+def _shape(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, n_quant_tok=1024, n_resid_tok=16,
+             cache_capacity=1024, resid_capacity=128, softmax_scale=0.0884)
+    d.update(kw)
+    return _lib.nsn_attn_shape(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=6, n_kv_heads=4), _lib.NSN_ERR_INVALID_ARG),
+    (dict(n_quant_tok=1000), _lib.NSN_ERR_INVALID_ARG),
+    (dict(cache_capacity=512), _lib.NSN_ERR_INVALID_ARG),
+    (dict(n_resid_tok=200), _lib.NSN_ERR_INVALID_ARG),
+    (dict(n_quant_tok=0, n_resid_tok=0), _lib.NSN_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), _lib.NSN_ERR_INVALID_ARG),
+    (dict(batch=0), _lib.NSN_ERR_INVALID_ARG),
+    (dict(n_resid_tok=2000, resid_capacity=4096), _lib.NSN_ERR_UNSUPPORTED),
+])
+def test_attention_validation(lib, kw, status):
+    s = _shape(**kw)
+    args = [FAKE] * 10
+    st = lib.nsn_decode_attention(P(), ctypes.byref(s), *args, FAKE, 1 << 30, FAKE, NULL)
+    assert st == status
+    assert lib.nsn_decode_attention_workspace_size(P(), ctypes.byref(s)) == 0
+
+
+def test_attention_workspace_size_and_check(lib):
+    s = _shape()
+    need = lib.nsn_decode_attention_workspace_size(P(), ctypes.byref(s))
+    assert need > 0 and need % 4 == 0
+    args = [FAKE] * 10
+    st = lib.nsn_decode_attention(P(), ctypes.byref(s), *args, FAKE, need - 4, FAKE, NULL)
+    assert st == _lib.NSN_ERR_WORKSPACE
+    st = lib.nsn_decode_attention(P(), ctypes.byref(s), *args, NULL, need, FAKE, NULL)
+    assert st == _lib.NSN_ERR_INVALID_ARG

@@ -1,0 +1,145 @@
+"""Parity of nsn_decode_attention (HIP, through the C ABI) with the oracle on
+the same cache bytes: max-abs error <= 2e-3 (the output is fp32)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import DEV, alloc_outputs, requires_gpu, table_for, torch
+from tests.parity import ATTN_ABS, rel_l2
+
+import kv_cache_calibration_amd as nsnq
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def build_cache(B, Hkv, Nq, R, m, G, seed, cap=None, rcap=None, device_gen=False):
+    """Quantize synthetic K/V (outlier model) into a cache with the library."""
+    cap = cap or max(Nq, G)
+    rcap = rcap or max(R, 1)
+    p, table, C = table_for(m, G)
+    n_seq = B * Hkv
+    if device_gen:
+        K, V = synth.kv_torch(n_seq, Nq + R, 5.0, seed, DEV)
+    else:
+        Kn, Vn = synth.kv_numpy(n_seq, Nq + R, 5.0, seed=seed)
+        K, V = torch.from_numpy(Kn).to(DEV), torch.from_numpy(Vn).to(DEV)
+    kc, km, ks = alloc_outputs(n_seq, cap, m, G)
+    vc, vm, vs = alloc_outputs(n_seq, cap, m, G)
+    if Nq:
+        nsnq.nsn_quantize(p, K[:, :Nq], table, kc, km, ks)
+        nsnq.nsn_quantize(p, V[:, :Nq], table, vc, vm, vs)
+    kr = torch.zeros((n_seq, rcap, 128), dtype=torch.float16, device=DEV)
+    vr = torch.zeros_like(kr)
+    kr[:, :R] = K[:, Nq:]
+    vr[:, :R] = V[:, Nq:]
+
+    def v4(t):
+        return t.view(B, Hkv, *t.shape[1:])
+    return dict(p=p, table=table, C=C, k=(v4(kc), v4(km), v4(ks)), v=(v4(vc), v4(vm), v4(vs)),
+                kr=v4(kr), vr=v4(vr), G=G, Nq=Nq, R=R)
+
+
+def run_gpu(cache, q, scale=None):
+    B, Hq, _ = q.shape
+    Hkv = cache["k"][0].shape[1]
+    scale = scale or 1.0 / math.sqrt(128)
+    p = cache["p"]
+    ws = nsnq.nsn_decode_attention_workspace_size(
+        p, B, Hq, Hkv, cache["Nq"], cache["R"], cache["k"][0].shape[2], cache["kr"].shape[2], scale)
+    work = torch.empty(max(ws, 16), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    nsnq.nsn_decode_attention(p, q, cache["k"], cache["v"], cache["kr"], cache["vr"],
+                              cache["table"], work, out, cache["Nq"], cache["R"], scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def to_np(cache):
+    f = lambda t: t.cpu().numpy()  # noqa: E731
+    return (tuple(f(t) for t in cache["k"]), tuple(f(t) for t in cache["v"]),
+            f(cache["kr"]), f(cache["vr"]))
+
+
+def check(cache, q, heads=None, scale=None):
+    scale = scale or 1.0 / math.sqrt(128)
+    got = run_gpu(cache, q, scale)
+    k, v, kr, vr = to_np(cache)
+    want = oracle.decode_attention(q.cpu().numpy(), k, v, kr, vr, cache["C"], cache["G"],
+                                   cache["Nq"], cache["R"], scale, heads=heads)
+    sel = np.isfinite(want)
+    err = np.abs(got[sel] - want[sel]).max()
+    assert err <= ATTN_ABS, err
+    assert rel_l2(got[sel], want[sel]) < 2e-3
+    return err
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,R,m,G", [
+    (2, 8, 2, 1024, 16, 4, 128),       # GQA 4:1
+    (1, 2, 2, 2048, 128, 4, 128),      # MHA
+    (1, 16, 2, 3072, 5, 4, 128),       # GQA 8:1 (two head blocks), ragged last tile
+    (2, 4, 2, 1536, 33, 4, 256),       # G = 256, GQA 2:1
+    (1, 8, 2, 2048, 64, 8, 128),       # 1-bit codes
+    (1, 4, 1, 10240, 7, 4, 128),       # several chunks, ragged chunk end
+])
+def test_attention_parity_small(B, Hq, Hkv, Nq, R, m, G):
+    print(f"attention B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} R={R} m={m} G={G}", flush=True)
+    cache = build_cache(B, Hkv, Nq, R, m, G, seed=31)
+    q = synth.query_torch((B, Hq, 128), seed=32, device=DEV)
+    check(cache, q)
+
+
+def test_attention_residual_only_and_quantized_only():
+    cache = build_cache(1, 2, 0, 100, 4, 128, seed=33)
+    q = synth.query_torch((1, 8, 128), seed=34, device=DEV)
+    check(cache, q)
+    cache = build_cache(1, 2, 1024, 0, 4, 128, seed=35)
+    check(cache, q)
+
+
+def test_attention_zero_query_is_mean_of_values():
+    cache = build_cache(1, 1, 512, 3, 4, 128, seed=36)
+    q = torch.zeros((1, 4, 128), dtype=torch.float16, device=DEV)
+    got = run_gpu(cache, q)
+    _, v, _, vr = to_np(cache)
+    vals = np.concatenate([oracle.dequantize(*(a[0, 0, :512] for a in v[:2]), v[2][0, 0, :4],
+                                             cache["C"], 128),
+                           vr[0, 0, :3].astype(np.float64)])
+    for h in range(4):
+        assert np.abs(got[0, h] - vals.mean(0)).max() <= ATTN_ABS
+
+
+def test_attention_large_scale_softmax_is_stable():
+    """A large softmax scale makes a few tokens dominate; still finite."""
+    cache = build_cache(1, 1, 2048, 16, 4, 128, seed=37)
+    q = synth.query_torch((1, 4, 128), seed=38, device=DEV)
+    check(cache, q, scale=2.0)
+
+
+def test_attention_decode_workload_sampled():
+    """The decode workload at full size: B=16, 32 q heads on 8 kv heads,
+    32768 quantized tokens + 128 fp16 residual tokens; sampled heads vs the
+    oracle on the same cache bytes."""
+    w = synth.WORKLOADS["decode"]
+    print("attention decode workload (full size, sampled heads)", flush=True)
+    cache = build_cache(w["B"], w["Hkv"], w["Nq"], w["R"], w["m"], w["G"], seed=w["seed"],
+                        device_gen=True)
+    q = synth.query_torch((w["B"], w["Hq"], 128), seed=w["seed"] + 1, device=DEV)
+    got = run_gpu(cache, q)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(0)
+    heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, w["B"], 4), rng.integers(0, w["Hq"], 4))]
+    heads += [(0, 0), (w["B"] - 1, w["Hq"] - 1)]
+    qn = q.cpu().numpy()
+    for b, h in heads:
+        kvh = h // (w["Hq"] // w["Hkv"])
+        sl = lambda t: t[b:b + 1, kvh:kvh + 1].cpu().numpy()  # noqa: E731
+        k = tuple(sl(t) for t in cache["k"])
+        v = tuple(sl(t) for t in cache["v"])
+        want = oracle.decode_attention(qn[b:b + 1, h:h + 1], k, v, sl(cache["kr"]), sl(cache["vr"]),
+                                       cache["C"], w["G"], w["Nq"], w["R"], 1 / math.sqrt(128))
+        err = np.abs(got[b, h] - want[0, 0]).max()
+        assert err <= ATTN_ABS, (b, h, err)
