@@ -256,22 +256,28 @@ def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
     except Exception:  # noqa: BLE001
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    n_tok = 4096
-    xs = x[:2, :n_tok].cpu().numpy().astype(np.float64)
-    t0 = time.perf_counter()
-    for s in range(2):
-        oracle.quantize(xs[s], C, G)
-    tq = time.perf_counter() - t0
-    q_rate = quant_bytes(2, n_tok, m, G) / tq            # bytes/s
+    # quantize sample: whole prefill sequences of 8192 tokens until ~10 s
+    n_tok = 8192
+    tq, n_q = 0.0, 0
+    while tq < 10.0 and n_q < 64:
+        xs = x[n_q, :n_tok].cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.quantize(xs, C, G)
+        tq += time.perf_counter() - t0
+        n_q += 1
+    q_rate = quant_bytes(n_q, n_tok, m, G) / tq            # bytes/s
     kc, vc, kr, vr, q = cache
     sl = lambda t: t[0:1, 0:1].cpu().numpy()  # noqa: E731
     k = tuple(sl(t) for t in kc)
     v = tuple(sl(t) for t in vc)
     qn = q[0:1, 0:4].cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.decode_attention(qn, k, v, sl(kr), sl(vr), C, G, Nq, R, scale)
-    ta = time.perf_counter() - t0
-    a_rate = (Nq * (2 * (128 // m) + 8) + 2 * (Nq // G) * 256 + 2 * R * 256) / ta
+    ta, n_a = 0.0, 0
+    while ta < 5.0 and n_a < 16:
+        t0 = time.perf_counter()
+        oracle.decode_attention(qn, k, v, sl(kr), sl(vr), C, G, Nq, R, scale)
+        ta += time.perf_counter() - t0
+        n_a += 1
+    a_rate = n_a * (Nq * (2 * (128 // m) + 8) + 2 * (Nq // G) * 256 + 2 * R * 256) / ta
     step_s = qb / q_rate + ab / a_rate
     log(f"cpu oracle: quantize {q_rate / 1e9:.4f} GB/s ({tq:.1f}s), attention "
         f"{a_rate / 1e9:.4f} GB/s ({ta:.1f}s)")
@@ -281,9 +287,9 @@ def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
         "cores": cores,
         "blas_threads": blas_threads,
         "kind": "oracle",
-        "sample": (f"oracle.quantize on 2 prefill sequences x {n_tok} tokens ({tq:.1f} s) and "
-                   f"oracle.decode_attention on one (batch, kv head) of the decode cache with its "
-                   f"4 q heads ({ta:.1f} s); step time extrapolated from the two rates"),
+        "sample": (f"oracle.quantize on {n_q} prefill sequences x {n_tok} tokens ({tq:.1f} s) and "
+                   f"oracle.decode_attention {n_a}x on one (batch, kv head) of the decode cache "
+                   f"with its 4 q heads ({ta:.1f} s); step time extrapolated from the two rates"),
         "quantize_gbps": q_rate / 1e9,
         "attention_gbps": a_rate / 1e9,
     }

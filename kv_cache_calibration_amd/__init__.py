@@ -72,7 +72,7 @@ def _dev(*ts):
 
 def _inner_contig(t, inner):
     """dims >= 1 contiguous with the given inner sizes."""
-    if tuple(t.shape[1:]) != tuple(inner) and inner is not None:
+    if inner is not None and tuple(t.shape[1:]) != tuple(inner):
         raise ValueError(f"expected inner shape {inner}, got {tuple(t.shape[1:])}")
     st = 1
     for d in range(t.dim() - 1, 0, -1):

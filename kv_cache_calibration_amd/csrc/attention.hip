@@ -7,18 +7,24 @@
 // Everything on quantized tokens happens in the rotated domain: with
 // q' = H q / sqrt(d) (computed once per workgroup),
 //   <q, x_hat_t> = s1_t (s2'_t <q', c(codes_t)> + <q', o'_g>),
-// so a key never has to be dequantized.  <q', c(codes_t)> is a sum over the
-// token's sub-vectors of a per-workgroup lookup table
-//   T[j][code][h] = <q'_h[m j : m j + m], C[code]>
-// (one LDS read of all heads' entries per code).  Values are accumulated in
-// the rotated domain too, and rotated back once per query head at the end.
+// so a key is never dequantized.  <q', c(codes_t)> is a sum over the token's
+// sub-vectors of a per-workgroup lookup table
+//   T[j][code] = ( <q'_h[m j : m j + m], C[code]> )_{h < 4}
+// (one 16-byte LDS read gives all four heads).  Values are accumulated in the
+// rotated domain and rotated back once per query head in the combine kernel.
 //
-// attn_split_kernel: one workgroup (1024 threads) per (token chunk, kv head,
-//   block of up to 4 query heads, batch).  Per 1024-token tile it scores
-//   every token (one thread per token), updates the running max, and
-//   accumulates p * s1 * s2' * c(codes) into per-thread rotated-domain
-//   accumulators (thread = 16-channel slice x token slot) plus the per-group
-//   shift term p * s1 * o'_g.  It writes (acc[128], max, sum) per head.
+// attn_split_kernel: one workgroup (16 waves) per (token chunk, kv head,
+//   block of up to 4 query heads, batch).  After the shared set-up (rotated
+//   queries, per-group <q', o'_g>, lookup table) every wave runs its own
+//   online softmax over 64-token tiles with no workgroup barrier:
+//     score phase  lane = token: table lookups, scale, wave max, exp;
+//                  weights w = p s1 s2' go to a per-wave LDS buffer (fp16);
+//     value phase  lane = (16-channel unit, token slot): tokens are taken in
+//                  pairs so one v_dot2_f32_f16 does w_a c_a + w_b c_b into an
+//                  fp32 accumulator (codewords are exact fp16 values);
+//     shift term   p s1 o'_g, from the wave-summed p s1 of the tile.
+//   The 16 wave partials are merged through LDS at the end and one
+//   (acc[128], max, sum) partial per head is written.
 // attn_combine_kernel: one workgroup per (kv head block, batch): the
 //   residual window's exact fp16 attention, a log-sum-exp merge with the
 //   chunk partials, one inverse rotation, normalization.
@@ -29,15 +35,15 @@ namespace nsn {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kTile = 1024;         // tokens per tile (one per thread in the score phase)
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kHB = 4;              // query heads per workgroup
 constexpr int kMaxChunk = 8192;     // quantized tokens per workgroup, at most
 constexpr int kMinChunk = 1024;
 constexpr int kPartStride = 132;    // acc[128], m, l, pad
-constexpr int kWaves = kThreads / kWave;
-constexpr int kSlots = kThreads / 8;  // token slots in the value phase
 constexpr float kInvSqrtD = 0.08838834764831845f;
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 struct SplitParams {
   const uint16_t* q;
@@ -54,25 +60,31 @@ struct SplitParams {
   float scale;
 };
 
-__device__ __forceinline__ uint32_t byte_of(const uint32_t (&w)[8], int j) {
-  return (w[j >> 2] >> (8 * (j & 3))) & 0xffu;
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
+}
+// (lo half of a, lo half of b) and (hi half of a, hi half of b)
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 template <int M, int G>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
   constexpr int NSUB = kD / M;
-  constexpr int CODE_BYTES = NSUB;              // bytes of codes per token
-  constexpr int UNIT_POS = 16 / M;              // sub-vector positions per 16-channel unit
+  constexpr int CODE_BYTES = NSUB;   // bytes of codes per token
+  constexpr int UPOS = 16 / M;       // sub-vector positions per 16-channel unit
+  constexpr int CW = M / 2;          // dwords per fp16 codeword
   constexpr int kMaxGroups = kMaxChunk / G;
-  constexpr int kTileGroups = kTile / G;
 
-  __shared__ float4 lut[NSUB * kCodes];         // T[j][code] -> 4 heads
-  __shared__ float cbs[kCodes * M];
+  __shared__ float4 lut[NSUB * kCodes];   // T[j][code] -> 4 heads (also the merge scratch)
+  __shared__ uint32_t cbh[kCodes * CW];   // fp16 codebook, CW dwords per code
   __shared__ float qr[kHB][kD];
-  __shared__ float4 wts[kTile];
   __shared__ float qo[kMaxGroups][kHB];
-  __shared__ float red[kWaves][kHB];
-  __shared__ float gred[kWaves][kHB];
+  __shared__ uint2 wbuf[kWaves][64];      // per-wave fp16 weights of the tile's tokens
+  __shared__ float wm[kWaves][kHB];       // per-wave running max, for the merge
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -87,9 +99,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
   const int c1 = min(p.n_quant, c0 + p.chunk);
   const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;  // (b, kvh) cache row
 
-  // ---- setup: codebook, rotated queries, per-group <q', o'_g>, lookup table
-  const float* cbg = reinterpret_cast<const float*>(p.table + kTabCodebook);
-  for (int i = tid; i < kCodes * M; i += kThreads) cbs[i] = cbg[i];
+  // ---- set-up: fp16 codebook, rotated queries, per-group <q', o'_g>, table
+  const uint32_t* cbg = reinterpret_cast<const uint32_t*>(p.table + kTabCodebookH);
+  for (int i = tid; i < kCodes * CW; i += kThreads) cbh[i] = cbg[i];
   if (tid < kHB * kD) {
     const int h = tid / kD, c = tid % kD;
     qr[h][c] = h < nh ? h2f(p.q[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c]) : 0.f;
@@ -118,35 +130,43 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
     s = wave_sum(s);
     if (lane == 0) qo[g][h] = s;
   }
-  for (int e = tid; e < NSUB * kCodes; e += kThreads) {
-    const int j = e / kCodes, k = e % kCodes;
-    float t[kHB];
+  {
+    const float* cbf = reinterpret_cast<const float*>(p.table + kTabCodebook);
+    for (int e = tid; e < NSUB * kCodes; e += kThreads) {
+      const int j = e / kCodes, k = e % kCodes;
+      float c[M];
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      float s = 0.f;
+      for (int i = 0; i < M; ++i) c[i] = cbf[k * M + i];
+      float t[kHB];
 #pragma unroll
-      for (int i = 0; i < M; ++i) s = fmaf(qr[h][M * j + i], cbs[k * M + i], s);
-      t[h] = s;
+      for (int h = 0; h < kHB; ++h) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < M; ++i) s = fmaf(qr[h][M * j + i], c[i], s);
+        t[h] = s;
+      }
+      lut[e] = make_float4(t[0], t[1], t[2], t[3]);
     }
-    lut[e] = make_float4(t[0], t[1], t[2], t[3]);
   }
   __syncthreads();
 
-  // ---- main loop
-  float m_run[kHB], l_part[kHB];
+  // ---- per-wave online softmax over 64-token tiles
+  const int u = lane & 7;        // 16-channel unit (value phase)
+  const int slot = lane >> 3;    // token slot (value phase)
+  const int sh_h = slot >> 1;                 // shift term: this lane's head
+  const int sh_c = 16 * u + 8 * (slot & 1);   // and its 8 channels
+  float m_run[kHB], l_lane[kHB];
+  float acc[kHB][16];
+  float sh[8];
 #pragma unroll
   for (int h = 0; h < kHB; ++h) {
     m_run[h] = -__builtin_huge_valf();
-    l_part[h] = 0.f;
-  }
-  float acc[kHB][16];
-#pragma unroll
-  for (int h = 0; h < kHB; ++h)
+    l_lane[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
-  float acc_sh = 0.f;  // shift term for (h, c) = (tid / 128, tid % 128), tid < 512
-  const int u = tid & 7;       // 16-channel unit of the value phase
-  const int slot = tid >> 3;   // token slot of the value phase
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sh[i] = 0.f;
 
   const uint8_t* kcrow = p.kc + row * p.cap * CODE_BYTES;
   const uint8_t* vcrow = p.vc + row * p.cap * CODE_BYTES;
@@ -154,124 +174,133 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
   const uint32_t* vmrow = reinterpret_cast<const uint32_t*>(p.vm + row * p.cap * 2);
   const uint16_t* vsrow = p.vs + row * (p.cap / G) * kD;
 
-  for (int t0 = c0; t0 < c1; t0 += kTile) {
-    // -- score phase: one thread per token
-    const int t = t0 + tid;
+  for (int t0 = c0 + 64 * wave; t0 < c1; t0 += 64 * kWaves) {
+    // -- score phase: lane = token
+    const int t = t0 + lane;
     const bool valid = t < c1;
-    float s[kHB];
-    float s1v = 0.f, s2v = 0.f;
+    uint32_t w8[8];
+    uint32_t kmv = 0, vmv = 0;
     if (valid) {
-      uint32_t w[8];
       const uint8_t* src = kcrow + static_cast<int64_t>(t) * CODE_BYTES;
 #pragma unroll
       for (int i = 0; i < CODE_BYTES / 16; ++i) {
         const u32x4 c = load_nt16(src + 16 * i);
-        w[4 * i] = c.x;
-        w[4 * i + 1] = c.y;
-        w[4 * i + 2] = c.z;
-        w[4 * i + 3] = c.w;
+        w8[4 * i] = c.x;
+        w8[4 * i + 1] = c.y;
+        w8[4 * i + 2] = c.z;
+        w8[4 * i + 3] = c.w;
       }
-      float4 dot = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int j = 0; j < NSUB; ++j) {
-        const float4 L = lut[j * kCodes + byte_of(w, j)];
-        dot.x += L.x;
-        dot.y += L.y;
-        dot.z += L.z;
-        dot.w += L.w;
-      }
-      const uint32_t kmv = __builtin_nontemporal_load(kmrow + t);
-      const uint32_t vmv = __builtin_nontemporal_load(vmrow + t);
-      const float s1k = h2f(kmv & 0xffffu), s2k = h2f(kmv >> 16);
-      s1v = h2f(vmv & 0xffffu);
-      s2v = h2f(vmv >> 16);
-      const int g = (t - c0) / G;
-      const float ks1 = p.scale * s1k;
-      s[0] = ks1 * fmaf(s2k, dot.x, qo[g][0]);
-      s[1] = ks1 * fmaf(s2k, dot.y, qo[g][1]);
-      s[2] = ks1 * fmaf(s2k, dot.z, qo[g][2]);
-      s[3] = ks1 * fmaf(s2k, dot.w, qo[g][3]);
+      kmv = __builtin_nontemporal_load(kmrow + t);
+      vmv = __builtin_nontemporal_load(vmrow + t);
     } else {
 #pragma unroll
-      for (int h = 0; h < kHB; ++h) s[h] = -__builtin_huge_valf();
+      for (int i = 0; i < 8; ++i) w8[i] = 0u;
     }
-    // tile max per head
+    float4 dot = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const uint32_t code = (w8[j >> 2] >> (8 * (j & 3))) & 0xffu;
+      const float4 L = lut[j * kCodes + code];
+      dot.x += L.x;
+      dot.y += L.y;
+      dot.z += L.z;
+      dot.w += L.w;
+      // keep at most 8 table reads in flight (register pressure)
+      if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    const int g = (t0 - c0) / G;  // one group per tile (64 divides G)
+    const float s1k = h2f(kmv & 0xffffu), s2k = h2f(kmv >> 16);
+    const float s1v = h2f(vmv & 0xffffu), s2v = h2f(vmv >> 16);
+    const float ks1 = p.scale * s1k;
+    float s[kHB];
+    s[0] = ks1 * fmaf(s2k, dot.x, qo[g][0]);
+    s[1] = ks1 * fmaf(s2k, dot.y, qo[g][1]);
+    s[2] = ks1 * fmaf(s2k, dot.z, qo[g][2]);
+    s[3] = ks1 * fmaf(s2k, dot.w, qo[g][3]);
+    float pw[kHB], gs[kHB];
 #pragma unroll
     for (int h = 0; h < kHB; ++h) {
-      const float mx = wave_max(s[h]);
-      if (lane == 0) red[wave][h] = mx;
-    }
-    __syncthreads();
-    float f[kHB], pw[kHB];
+      if (!valid) s[h] = -__builtin_huge_valf();
+      const float mnew = fmaxf(m_run[h], wave_max(s[h]));  // wave-uniform
+      if (mnew > m_run[h]) {
+        const float f = __expf(m_run[h] - mnew);
+        m_run[h] = mnew;
+        l_lane[h] *= f;
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      float mx = red[0][h];
+        for (int i = 0; i < 16; ++i) acc[h][i] *= f;
+        if (sh_h == h) {
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, red[w][h]);
-      const float mnew = fmaxf(m_run[h], mx);
-      f[h] = __expf(m_run[h] - mnew);
-      m_run[h] = mnew;
-      pw[h] = valid ? __expf(s[h] - mnew) : 0.f;
-      l_part[h] = fmaf(l_part[h], f[h], pw[h]);
-    }
-    wts[tid] = make_float4(pw[0] * s1v * s2v, pw[1] * s1v * s2v, pw[2] * s1v * s2v,
-                           pw[3] * s1v * s2v);
-    // per-group sums of p * s1 for the shift term (a group spans G/64 waves)
-#pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      const float gs = wave_sum(pw[h] * s1v);
-      if (lane == 0) gred[wave][h] = gs;
-    }
-    __syncthreads();
-    if (tid < kHB * kD) {
-      const int h = tid / kD, c = tid % kD;
-      float a = acc_sh * f[h];
-      const int gt0 = (t0 - c0) / G;
-      for (int gg = 0; gg < kTileGroups; ++gg) {
-        if (t0 + gg * G >= c1) break;
-        float gs = 0.f;
-#pragma unroll
-        for (int w = 0; w < G / kWave; ++w) gs += gred[gg * (G / kWave) + w][h];
-        a = fmaf(gs, h2f(vsrow[static_cast<int64_t>(c0 / G + gt0 + gg) * kD + c]), a);
+          for (int i = 0; i < 8; ++i) sh[i] *= f;
+        }
       }
-      acc_sh = a;
+      pw[h] = valid ? __expf(s[h] - m_run[h]) : 0.f;
+      l_lane[h] += pw[h];
+      gs[h] = wave_sum(pw[h] * s1v);
     }
-    // -- value phase: thread = (16-channel unit u, token slot)
+    const float sv = s1v * s2v;
+    wbuf[wave][lane] = make_uint2(
+        static_cast<uint32_t>(f2h(pw[0] * sv)) | (static_cast<uint32_t>(f2h(pw[1] * sv)) << 16),
+        static_cast<uint32_t>(f2h(pw[2] * sv)) | (static_cast<uint32_t>(f2h(pw[3] * sv)) << 16));
+    // shift term p s1 o'_g: this lane owns head sh_h, channels sh_c .. sh_c + 7
+    {
+      const u32x4 o = load_nt16(vsrow + static_cast<int64_t>(c0 / G + g) * kD + sh_c);
+      const float gsh = sh_h == 0 ? gs[0] : sh_h == 1 ? gs[1] : sh_h == 2 ? gs[2] : gs[3];
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-    for (int h = 0; h < kHB; ++h)
+      for (int i = 0; i < 4; ++i) {
+        sh[2 * i] = fmaf(gsh, h2f(ow[i] & 0xffffu), sh[2 * i]);
+        sh[2 * i + 1] = fmaf(gsh, h2f(ow[i] >> 16), sh[2 * i + 1]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // -- value phase: lane = (unit u, slot); token pairs (a, a + 8)
+#pragma unroll 2
+    for (int k = 0; k < 4; ++k) {
+      const int ia = slot + 16 * k, ib = ia + 8;
+      const int ta = t0 + ia, tb = t0 + ib;
+      uint32_t va = 0, vb = 0;
+      if constexpr (M == 4) {
+        if (ta < c1) va = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcrow + static_cast<int64_t>(ta) * CODE_BYTES) + u);
+        if (tb < c1) vb = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcrow + static_cast<int64_t>(tb) * CODE_BYTES) + u);
+      } else {
+        if (ta < c1) va = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(vcrow + static_cast<int64_t>(ta) * CODE_BYTES) + u);
+        if (tb < c1) vb = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(vcrow + static_cast<int64_t>(tb) * CODE_BYTES) + u);
+      }
+      const uint2 wa = wbuf[wave][ia], wb = wbuf[wave][ib];
+      const uint32_t wp[kHB] = {pair_lo(wa.x, wb.x), pair_hi(wa.x, wb.x), pair_lo(wa.y, wb.y),
+                                pair_hi(wa.y, wb.y)};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[h][i] *= f[h];
-    for (int i = 0; i < kTile / kSlots; ++i) {
-      const int tt = t0 + slot + kSlots * i;
-      if (tt >= c1) break;
-      const float4 wv = wts[tt - t0];
-      uint32_t cw;
-      if constexpr (M == 4)
-        cw = __builtin_nontemporal_load(
-            reinterpret_cast<const uint32_t*>(vcrow + static_cast<int64_t>(tt) * CODE_BYTES) + u);
-      else
-        cw = __builtin_nontemporal_load(
-            reinterpret_cast<const uint16_t*>(vcrow + static_cast<int64_t>(tt) * CODE_BYTES) + u);
+      for (int pos = 0; pos < UPOS; ++pos) {
+        const uint32_t ca = (va >> (8 * pos)) & 0xffu, cb = (vb >> (8 * pos)) & 0xffu;
+        uint32_t xa[CW], xb[CW];
 #pragma unroll
-      for (int pos = 0; pos < UNIT_POS; ++pos) {
-        const int code = (cw >> (8 * pos)) & 0xff;
+        for (int i = 0; i < CW; ++i) {
+          xa[i] = cbh[ca * CW + i];
+          xb[i] = cbh[cb * CW + i];
+        }
 #pragma unroll
-        for (int e = 0; e < M; ++e) {
-          const float c = cbs[code * M + e];
-          acc[0][pos * M + e] = fmaf(wv.x, c, acc[0][pos * M + e]);
-          acc[1][pos * M + e] = fmaf(wv.y, c, acc[1][pos * M + e]);
-          acc[2][pos * M + e] = fmaf(wv.z, c, acc[2][pos * M + e]);
-          acc[3][pos * M + e] = fmaf(wv.w, c, acc[3][pos * M + e]);
+        for (int i = 0; i < CW; ++i) {
+          const uint32_t plo = pair_lo(xa[i], xb[i]), phi = pair_hi(xa[i], xb[i]);
+#pragma unroll
+          for (int h = 0; h < kHB; ++h) {
+            acc[h][pos * M + 2 * i] = dot2(wp[h], plo, acc[h][pos * M + 2 * i]);
+            acc[h][pos * M + 2 * i + 1] = dot2(wp[h], phi, acc[h][pos * M + 2 * i + 1]);
+          }
         }
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- reductions and partial output
-  // sum over token slots: lanes with equal u inside a wave, then over waves
+  // ---- merge: slots inside each wave, then the 16 waves
 #pragma unroll
-  for (int h = 0; h < kHB; ++h)
+  for (int h = 0; h < kHB; ++h) {
+    l_lane[h] = wave_sum(l_lane[h]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float v = acc[h][i];
@@ -280,33 +309,46 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
       v += __shfl_xor(v, 32, kWave);
       acc[h][i] = v;
     }
-  float* racc = reinterpret_cast<float*>(lut);  // [kWaves][8 units][64]
-  if (lane < 8) {
+  }
+  __syncthreads();  // every wave is done with the lookup table
+  float* wacc = reinterpret_cast<float*>(lut);        // [kWaves][4][128]
+  float* wl = wacc + kWaves * kHB * kD;               // [kWaves][4]
+  if (slot == 0) {
 #pragma unroll
     for (int h = 0; h < kHB; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) racc[(wave * 8 + lane) * 64 + h * 16 + i] = acc[h][i];
+      for (int i = 0; i < 16; ++i) wacc[(wave * kHB + h) * kD + 16 * u + i] = acc[h][i];
   }
+  if (lane == 0) {
 #pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    const float ls = wave_sum(l_part[h]);
-    if (lane == 0) red[wave][h] = ls;
+    for (int h = 0; h < kHB; ++h) {
+      wm[wave][h] = m_run[h];
+      wl[wave * kHB + h] = l_lane[h];
+    }
   }
+  __syncthreads();
+  // the shift-term accumulators: each (head, channel) of a wave's row has
+  // exactly one owner lane, so a plain read-modify-write is race free
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wacc[(wave * kHB + sh_h) * kD + sh_c + i] += sh[i];
   __syncthreads();
   if (tid < kHB * kD) {
     const int h = tid / kD, c = tid % kD;
-    const int uu = c / 16, ii = c % 16;
-    float a = acc_sh;
+    float M_ = -__builtin_huge_valf();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) a += racc[(w * 8 + uu) * 64 + h * 16 + ii];
+    for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, wm[w][h]);
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = wm[w][h] == -__builtin_huge_valf() ? 0.f : __expf(wm[w][h] - M_);
+      a = fmaf(e, wacc[(w * kHB + h) * kD + c], a);
+      l = fmaf(e, wl[w * kHB + h], l);
+    }
     if (h < nh) {
       float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * p.n_split + split) * kPartStride;
       dst[c] = a;
       if (c == 0) {
-        float l = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) l += red[w][h];
-        dst[128] = m_run[h];
+        dst[128] = M_;
         dst[129] = l;
       }
     }

@@ -168,3 +168,20 @@ def test_attention_workspace_size_and_check(lib):
     assert st == _lib.NSN_ERR_WORKSPACE
     st = lib.nsn_decode_attention(P(), ctypes.byref(s), *args, NULL, need, FAKE, NULL)
     assert st == _lib.NSN_ERR_INVALID_ARG
+
+
+def test_binding_inner_layout_checks():
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    t = torch.zeros((4, 256, 32), dtype=torch.uint8)
+    nsnq._inner_contig(t, None)
+    nsnq._inner_contig(t[:, 128:], None)          # a group-offset view of a cache
+    nsnq._inner_contig(t, (256, 32))
+    with pytest.raises(ValueError):
+        nsnq._inner_contig(t, (256, 16))
+    with pytest.raises(ValueError):
+        nsnq._inner_contig(t[:, :, :16], None)     # inner dim not contiguous
+    with pytest.raises(ValueError):
+        nsnq._dev(t)                              # host tensors are rejected
+    p = nsnq.Params(sub_dim=8, group_size=256, scale_adjust=False)
+    assert (p.c.sub_dim, p.c.group_size, p.c.flags, p.c.head_dim) == (8, 256, 0, 128)
