@@ -103,6 +103,19 @@ nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook,
                                 void* stream);
 
 /*
+ * nsn_nearest_codeword -- index of the nearest codeword of each of n
+ * arbitrary sub-vectors, through the same search the quantizer uses.
+ * [NSNQuant summary §3: each rotated sub-vector is replaced by its nearest
+ *  codeword in one global codebook.]
+ * v      device float32 [n][sub_dim]; out device uint8 [n].
+ * Nearest = smallest exact squared distance in float32, lowest index among
+ * equal distances.  Requires n >= 0.
+ */
+nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table,
+                                const float* v, int64_t n, uint8_t* out,
+                                void* stream);
+
+/*
  * nsn_quantize -- compress whole token groups.
  * [NSNQuant summary §1 (Normalize, Shift over the group, Normalize),
  *  §2 (Hadamard rotation), §3 (nearest codeword, scale adjustment),

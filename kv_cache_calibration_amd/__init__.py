@@ -25,6 +25,7 @@ __all__ = [
     "nsn_table_size",
     "nsn_build_codebook",
     "nsn_prepare_codebook",
+    "nsn_nearest_codeword",
     "nsn_quantize",
     "nsn_dequantize",
     "nsn_residual_append",
@@ -109,6 +110,21 @@ def nsn_prepare_codebook(params, codebook, table, stream=None):
     _lib.check(_lib.load().nsn_prepare_codebook(ctypes.byref(params.c), _ptr(codebook),
                                                 _ptr(table), table.numel() * table.element_size(),
                                                 _stream(stream)))
+
+
+def nsn_nearest_codeword(params, table, v, out, stream=None):
+    """Nearest codeword index of every row of v (float32 (n, sub_dim)) -> out uint8 (n,)."""
+    import torch
+    _dev(table, v, out)
+    if v.dtype != torch.float32 or out.dtype != torch.uint8:
+        raise ValueError("v must be float32 and out uint8")
+    if not v.is_contiguous() or not out.is_contiguous() or v.shape[-1] != params.sub_dim:
+        raise ValueError("v must be contiguous (n, sub_dim) and out contiguous (n,)")
+    n = v.numel() // params.sub_dim
+    if out.numel() < n:
+        raise ValueError("out too small")
+    _lib.check(_lib.load().nsn_nearest_codeword(ctypes.byref(params.c), _ptr(table), _ptr(v), n,
+                                                _ptr(out), _stream(stream)))
 
 
 def _dtype_code(t):

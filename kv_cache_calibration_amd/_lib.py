@@ -55,6 +55,7 @@ SIGNATURES = {
     "nsn_build_codebook_workspace_size": (_SZ, [_I32, _I32, _I64]),
     "nsn_build_codebook": (_ST, [_I32, _I32, _I64, _I32, _P, _P, _P, _SZ, _P]),
     "nsn_prepare_codebook": (_ST, [ctypes.POINTER(nsn_params), _P, _P, _SZ, _P]),
+    "nsn_nearest_codeword": (_ST, [ctypes.POINTER(nsn_params), _P, _P, _I64, _P, _P]),
     "nsn_quantize": (_ST, [ctypes.POINTER(nsn_params), _ST, _P, _I64, _I64, _I64, _P,
                            _P, _I64, _P, _I64, _P, _I64, _P]),
     "nsn_dequantize": (_ST, [ctypes.POINTER(nsn_params), _P, _I64, _P, _I64, _P, _I64, _P,

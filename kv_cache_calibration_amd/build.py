@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnsn.so")
 
-SOURCES = ["nsn_api.hip", "quantize.hip", "attention.hip", "codebook.hip", "residual.hip"]
+SOURCES = ["nsn_api.hip", "quantize.hip", "quantize_mfma.hip", "search_table.hip", "attention.hip",
+           "codebook.hip", "residual.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -154,10 +154,13 @@ hipError_t launch_build_codebook(int sub_dim, int n_codes, int64_t n, int iters,
 hipError_t launch_prepare_codebook(const float* codebook, int sub_dim, void* table,
                                    hipStream_t s) {
   uint8_t* t = static_cast<uint8_t*>(table);
-  if (sub_dim == 4)
+  if (sub_dim == 4) {
     hipLaunchKernelGGL(prepare_kernel<4>, dim3(1), dim3(256), 0, s, codebook, t);
-  else
-    hipLaunchKernelGGL(prepare_kernel<8>, dim3(1), dim3(256), 0, s, codebook, t);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_search_table(table, s);
+  }
+  hipLaunchKernelGGL(prepare_kernel<8>, dim3(1), dim3(256), 0, s, codebook, t);
   return hipGetLastError();
 }
 

@@ -118,6 +118,23 @@ nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook, void
                     "nsn_prepare_codebook launch");
 }
 
+nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table, const float* v, int64_t n,
+                                uint8_t* out, void* stream) {
+  NSN_TRY(check_params(p));
+  if (n < 0) return fail(NSN_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) {
+    g_err[0] = '\0';
+    return NSN_OK;
+  }
+  if (n > (int64_t(1) << 36)) return fail(NSN_ERR_UNSUPPORTED, "n too large");
+  if (!table || !v || !out) return fail(NSN_ERR_INVALID_ARG, "table, v and out must be non-NULL");
+  if (!aligned16(table) || !aligned16(v) || !aligned16(out))
+    return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  return hip_status(nsn::launch_nearest(table, p->sub_dim, v, n, out,
+                                        static_cast<hipStream_t>(stream)),
+                    "nsn_nearest_codeword launch");
+}
+
 nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype, const void* x, int64_t n_seq,
                         int64_t n_tok, int64_t x_seq_stride, const void* table, uint8_t* codes,
                         int64_t codes_seq_stride, uint16_t* meta, int64_t meta_seq_stride,

@@ -16,10 +16,30 @@ constexpr int kWave = 64;
 //   [8192, 9216)     float32 squared norms [256]
 //   [9216, 13312)    fp16 codebook [256][m] (exact: entries are fp16 values
 //                    when built by nsn_build_codebook; otherwise rounded)
+//   [16384, 17408)   u8 bin of each fine cell of [-4.5, 4.5) (1024 cells)
+//   [17408, 17508)   float32 bin edges [25]
+//   kTabMain         u32 per 4-d grid cell: four candidate codes
+//   kTabExt          u32 per cell: (pool offset << 8 | extra count), or
+//                    kExtBrute when the cell's list did not fit the pool
+//   kTabPool         u8 extra candidates of cells with more than four
+// The 4-d search tables exist for m = 4 only.
 constexpr size_t kTabCodebook = 0;
 constexpr size_t kTabNorm2 = 8192;
 constexpr size_t kTabCodebookH = 9216;
-constexpr size_t kTabBytes = 16384;
+constexpr size_t kTabBinLut = 16384;
+constexpr size_t kTabEdges = 17408;
+constexpr int kNB = 24;                          // quantile bins per coordinate
+constexpr int kCells = kNB * kNB * kNB * kNB;    // 331776
+constexpr int kFine = 1024;                      // fine cells of [-4.5, 4.5)
+constexpr float kGridLo = -4.5f;
+constexpr float kFineW = 9.0f / 1024.0f;         // exact binary fraction
+constexpr float kFineInv = 1024.0f / 9.0f;
+constexpr size_t kTabMain = 18432;
+constexpr size_t kTabExt = kTabMain + size_t(kCells) * 4;
+constexpr size_t kTabPool = kTabExt + size_t(kCells) * 4;
+constexpr size_t kPoolBytes = size_t(4) << 20;
+constexpr size_t kTabBytes = kTabPool + kPoolBytes;
+constexpr uint32_t kExtBrute = 0xffffffffu;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -22,6 +22,11 @@ struct QuantArgs {
   int sub_dim, group_size, scale_adjust;
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+bool quantize_mfma_supported(int in_f32, int sub_dim, int group_size);
+hipError_t launch_quantize_mfma(const QuantArgs& a, hipStream_t s);
+hipError_t launch_search_table(void* table, hipStream_t s);
+hipError_t launch_nearest(const void* table, int sub_dim, const float* v, int64_t n, uint8_t* out,
+                          hipStream_t s);
 
 struct DequantArgs {
   const uint8_t* codes;

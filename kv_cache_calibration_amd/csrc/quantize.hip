@@ -269,6 +269,7 @@ hipError_t dequant_g(const DequantArgs& a, hipStream_t s) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.n_seq == 0 || a.n_tok == 0) return hipSuccess;
+  if (quantize_mfma_supported(a.in_f32, a.sub_dim, a.group_size)) return launch_quantize_mfma(a, s);
   if (a.in_f32) return a.sub_dim == 4 ? quant_g<float, 4>(a, s) : quant_g<float, 8>(a, s);
   return a.sub_dim == 4 ? quant_g<__half, 4>(a, s) : quant_g<__half, 8>(a, s);
 }
