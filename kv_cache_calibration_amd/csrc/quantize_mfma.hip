@@ -42,7 +42,7 @@ constexpr float kSqrtD = 11.313708498984761f;
 
 struct QEntry {
   float h[4];
-  uint32_t slot;   // token * 32 + sub-vector
+  uint32_t slot;   // sub-vector * 32 + token
   int32_t cell;    // -1: off the grid (full scan)
 };
 
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
   __shared__ float ascale[kG];
   __shared__ float csum[kNW][kD];
   __shared__ __attribute__((aligned(16))) float osh[kD];
-  __shared__ uint64_t res[kNW][32 * 32];
+  __shared__ uint64_t res[kNW][32 * 32];   // [sub-vector][token]: lanes hit distinct banks
   __shared__ QEntry queue[kNW][kQCap];
 
   const int tid = threadIdx.x;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
       }
       cell[q] = min(c, kCells - 1);   // in bounds even for an unprepared table
       off[q] = o;
-      mainv[q] = o ? 0u : __builtin_nontemporal_load(tmain + c);
+      mainv[q] = o ? 0u : tmain[cell[q]];
     }
     uint32_t flagged = 0;
 #pragma unroll
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
         best = key < best ? key : best;
       }
       const int j = 8 * mb + 2 * q + hf;
-      myres[t * 32 + j] = best;
+      myres[j * 32 + t] = best;
       const bool over = off[q] || ((mainv[q] & 0xffu) > ((mainv[q] >> 8) & 0xffu));
       flagged |= over ? (1u << q) : 0u;
     }
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
         e.h[1] = acc[mb][4 * q + 1];
         e.h[2] = acc[mb][4 * q + 2];
         e.h[3] = acc[mb][4 * q + 3];
-        e.slot = static_cast<uint32_t>(t * 32 + 8 * mb + 2 * q + hf);
+        e.slot = static_cast<uint32_t>((8 * mb + 2 * q + hf) * 32 + t);
         e.cell = off[q] ? -1 : cell[q];
         myq[rank] = e;
       }
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t k = static_cast<uint32_t>(myres[t * 32 + 8 * mb + 2 * q + hf]) & 0xffu;
+      const uint32_t k = static_cast<uint32_t>(myres[(8 * mb + 2 * q + hf) * 32 + t]) & 0xffu;
       const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * k]);
       const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
     uint32_t v = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
-      v |= (static_cast<uint32_t>(myres[t * 32 + 16 * hf + 4 * i + b]) & 0xffu) << (8 * b);
+      v |= (static_cast<uint32_t>(myres[(16 * hf + 4 * i + b) * 32 + t]) & 0xffu) << (8 * b);
     pk[i] = v;
   }
   *reinterpret_cast<u32x4*>(codes + seq * codes_seq_stride + tok * 32 + 16 * hf) =
