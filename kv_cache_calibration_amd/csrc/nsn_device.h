@@ -18,10 +18,7 @@ constexpr int kWave = 64;
 //                    when built by nsn_build_codebook; otherwise rounded)
 //   [16384, 17408)   u8 bin of each fine cell of [-4.5, 4.5) (1024 cells)
 //   [17408, 17508)   float32 bin edges [25]
-//   kTabMain         u32 per 4-d grid cell: four candidate codes
-//   kTabExt          u32 per cell: (pool offset << 8 | extra count), or
-//                    kExtBrute when the cell's list did not fit the pool
-//   kTabPool         u8 extra candidates of cells with more than four
+//   kTabMain         u64 per 4-d grid cell: eight candidate codes (below)
 // The 4-d search tables exist for m = 4 only.
 constexpr size_t kTabCodebook = 0;
 constexpr size_t kTabNorm2 = 8192;
@@ -35,11 +32,20 @@ constexpr float kGridLo = -4.5f;
 constexpr float kFineW = 9.0f / 1024.0f;         // exact binary fraction
 constexpr float kFineInv = 1024.0f / 9.0f;
 constexpr size_t kTabMain = 18432;
-constexpr size_t kTabExt = kTabMain + size_t(kCells) * 4;
-constexpr size_t kTabPool = kTabExt + size_t(kCells) * 4;
-constexpr size_t kPoolBytes = size_t(4) << 20;
-constexpr size_t kTabBytes = kTabPool + kPoolBytes;
-constexpr uint32_t kExtBrute = 0xffffffffu;
+constexpr size_t kTabBytes = kTabMain + size_t(kCells) * 8;
+
+// Candidate word of a grid cell (little-endian bytes b0..b7):
+//  * <= 4 candidates: b0..b3 ascending, padded by repeating the last; b4..b7 = b0..b3
+//  * 5..8: b0..b3 = the four lowest, stored descending (b0 > b1 flags "more
+//          than four"); b4..b7 the rest ascending, padded by repeating the last
+//  * > 8:  as 5..8 for the first eight, but b4..b7 stored descending
+//          (b4 > b5 flags "more than eight": the caller scans all codes)
+__device__ __forceinline__ bool cand_more_than_4(uint64_t w) {
+  return (w & 0xffu) > ((w >> 8) & 0xffu);
+}
+__device__ __forceinline__ bool cand_more_than_8(uint64_t w) {
+  return ((w >> 32) & 0xffu) > ((w >> 40) & 0xffu);
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

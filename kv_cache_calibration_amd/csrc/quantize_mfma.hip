@@ -18,12 +18,13 @@
 //    the channel-major pass weighted by 1/s1 (exactly the pages' Shift, since
 //    the rotation is linear and orthonormal), z = y - o', s2 = ||z||/sqrt(d).
 // 3. Nearest codeword: the sub-vector's box in the 24^4 quantile grid gives
-//    four candidate codes (one L2-resident u32); the exact squared distance
-//    in fp32 and a lexicographic (distance bits, code) key pick the lowest
-//    code among equal distances.  Boxes with more candidates and points off
-//    the grid go to a per-wave LDS queue, finished cooperatively (extra
-//    candidates from the pool, or a full scan) with an LDS 64-bit atomic min
-//    on the same key.
+//    up to eight candidate codes (one L2-resident u64); the first four are
+//    evaluated in place with the exact squared distance in fp32, lowest code
+//    first so ties keep the lowest index.  Sub-vectors whose box has five to
+//    eight candidates go to a per-wave LDS queue and are finished one per
+//    lane; boxes with more than eight and points off the grid are scanned over
+//    all codes by the whole wave.  Queue results are merged back with the
+//    same lexicographic (distance, code) order.
 // 4. Scale adjustment alpha = ||h||^2 / <h, h_hat>, codes, (s1, s2'), o'.
 #include "nsn_device.h"
 #include "nsn_launch.h"
@@ -40,10 +41,11 @@ constexpr int kNW = kG / 32;       // waves per workgroup
 constexpr int kQCap = 256;         // overflow queue entries per wave
 constexpr float kSqrtD = 11.313708498984761f;
 
-struct QEntry {
+struct alignas(16) QEntry {
   float h[4];
-  uint32_t slot;   // sub-vector * 32 + token
-  int32_t cell;    // -1: off the grid (full scan)
+  uint32_t codes;  // candidates five to eight (queue A)
+  uint32_t pad;
+  uint64_t res;    // lexicographic (distance, code) minimum, written back
 };
 
 __device__ __forceinline__ uint64_t dist_key(float d, uint32_t code) {
@@ -57,17 +59,16 @@ __device__ __forceinline__ float sqdist4(const float* h, const float* c) {
 
 __device__ __forceinline__ v8h as_v8h(u32x4 v) { return __builtin_bit_cast(v8h, v); }
 
-__global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
+__global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
     const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
     const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
     uint16_t* __restrict__ meta, int64_t meta_seq_stride, uint16_t* __restrict__ shift,
     int64_t shift_seq_stride, int scale_adjust) {
   __shared__ __attribute__((aligned(16))) float cb[kCodes * 4];
-  __shared__ __attribute__((aligned(16))) uint8_t binlut[kFine];
+  __shared__ __attribute__((aligned(16))) uint8_t binlut[3 * kFine];   // sentinels around the grid
   __shared__ float ascale[kG];
   __shared__ float csum[kNW][kD];
   __shared__ __attribute__((aligned(16))) float osh[kD];
-  __shared__ uint64_t res[kNW][32 * 32];   // [sub-vector][token]: lanes hit distinct banks
   __shared__ QEntry queue[kNW][kQCap];
 
   const int tid = threadIdx.x;
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
     for (int i = tid; i < kCodes * 4; i += kG * 2) cb[i] = cbg[i];
     const uint32_t* bl = reinterpret_cast<const uint32_t*>(table + kTabBinLut);
     uint32_t* bd = reinterpret_cast<uint32_t*>(binlut);
-    for (int i = tid; i < kFine / 4; i += kG * 2) bd[i] = bl[i];
+    for (int i = tid; i < 3 * kFine / 4; i += kG * 2)
+      bd[i] = (i >= kFine / 4 && i < 2 * kFine / 4) ? bl[i - kFine / 4] : 0x80808080u;
   }
 
   // ---- operands: x (fp16, 8 x 16 bytes per lane) and the H16 sign pattern
@@ -187,131 +189,179 @@ __global__ __launch_bounds__(kG * 2) void quantize_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] *= inv2;   // h
 
-  // ---- nearest codeword, four sub-vectors (one mb block) at a time
-  const uint32_t* tmain = reinterpret_cast<const uint32_t*>(table + kTabMain);
-  const uint32_t* text = reinterpret_cast<const uint32_t*>(table + kTabExt);
-  const uint8_t* tpool = table + kTabPool;
-  uint64_t* myres = res[w];
+  // ---- nearest codeword, four sub-vectors (one mb block) per step; the
+  //      candidate words of the next block are fetched while the current one
+  //      is evaluated.
+  const uint64_t* tmain = reinterpret_cast<const uint64_t*>(table + kTabMain);
   QEntry* myq = queue[w];
+  auto locate = [&](int mb, int q, bool& off) -> int {
+    uint32_t bins[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // fine index + 1024; off-grid and non-finite values land on sentinels
+      const uint32_t fi = static_cast<uint32_t>(
+          static_cast<int>(fmaf(acc[mb][4 * q + e], kFineInv, 512.0f + kFine)));
+      bins[e] = binlut[min(fi, static_cast<uint32_t>(3 * kFine - 1))];
+    }
+    off = ((bins[0] | bins[1] | bins[2] | bins[3]) & 0x80u) != 0;
+    return min(static_cast<int>(((bins[0] * kNB + bins[1]) * kNB + bins[2]) * kNB + bins[3]),
+               kCells - 1);
+  };
+  bool offv[2][4];
+  uint64_t wordv[2][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wordv[0][q] = tmain[locate(0, q, offv[0][q])];
+
+  float bestd[16];
+  uint32_t codes4[4] = {0u, 0u, 0u, 0u};   // best code of sub-vector k in byte k%4 of word k/4
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    int cell[4];
-    bool off[4];
-    uint32_t mainv[4];
+    const int cur = mb & 1, nxt = cur ^ 1;
+    if (mb < 3) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int c = 0;
-      bool o = false;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float fe = floorf(fmaf(acc[mb][4 * q + e], kFineInv, 512.0f));
-        o |= !(fe >= 0.f && fe < static_cast<float>(kFine));   // also catches NaN
-        const int fi = o ? 0 : static_cast<int>(fe);
-        c = c * kNB + binlut[fi];
-      }
-      cell[q] = min(c, kCells - 1);   // in bounds even for an unprepared table
-      off[q] = o;
-      mainv[q] = o ? 0u : tmain[cell[q]];
+      for (int q = 0; q < 4; ++q) wordv[nxt][q] = tmain[locate(mb + 1, q, offv[nxt][q])];
     }
-    uint32_t flagged = 0;
+    int na = 0, nb = 0;     // queue A (five to eight candidates), B (full scan)
+    int rank[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      const int k = 4 * mb + q;
       const float hv[4] = {acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
-      uint64_t best = ~uint64_t(0);
+      const uint64_t wv = wordv[cur][q];
+      const uint32_t lo = static_cast<uint32_t>(wv);
+      const bool more4 = cand_more_than_4(wv);
+      const bool scan = offv[cur][q] || cand_more_than_8(wv);
+      // the four lowest candidates in ascending code order, so a strict '<'
+      // keeps the lowest code among equal distances
+      const uint32_t asc = more4 ? __builtin_amdgcn_perm(0u, lo, 0x00010203u) : lo;
+      float bd = __builtin_huge_valf();
+      uint32_t bc = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t k = (mainv[q] >> (8 * i)) & 0xffu;
-        const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * k]);
+        const uint32_t code = (asc >> (8 * i)) & 0xffu;
+        const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
         const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-        const uint64_t key = dist_key(sqdist4(hv, cv), k);
-        best = key < best ? key : best;
+        const float d = sqdist4(hv, cv);
+        bc = d < bd ? code : bc;
+        bd = d < bd ? d : bd;
       }
-      const int j = 8 * mb + 2 * q + hf;
-      myres[j * 32 + t] = best;
-      const bool over = off[q] || ((mainv[q] & 0xffu) > ((mainv[q] >> 8) & 0xffu));
-      flagged |= over ? (1u << q) : 0u;
-    }
-    // push overflow entries (wave-uniform bookkeeping, no atomics)
-    int qn = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool over = (flagged >> q) & 1u;
-      const uint64_t bal = __ballot(over);
-      if (over) {
-        const int rank = qn + __popcll(bal & ((uint64_t(1) << lane) - 1));
+      if (scan) bd = __builtin_huge_valf();   // the full scan decides
+      bestd[k] = bd;
+      codes4[mb] |= bc << (8 * q);
+      const bool qa = more4 && !scan;
+      const uint64_t ba = __ballot(qa), bb = __ballot(scan);
+      const uint64_t below = (uint64_t(1) << lane) - 1;
+      rank[q] = qa ? na + __popcll(ba & below) : (scan ? kQCap - 1 - (nb + __popcll(bb & below)) : -1);
+      if (qa || scan) {
         QEntry e;
-        e.h[0] = acc[mb][4 * q];
-        e.h[1] = acc[mb][4 * q + 1];
-        e.h[2] = acc[mb][4 * q + 2];
-        e.h[3] = acc[mb][4 * q + 3];
-        e.slot = static_cast<uint32_t>((8 * mb + 2 * q + hf) * 32 + t);
-        e.cell = off[q] ? -1 : cell[q];
-        myq[rank] = e;
+        e.h[0] = hv[0];
+        e.h[1] = hv[1];
+        e.h[2] = hv[2];
+        e.h[3] = hv[3];
+        e.codes = static_cast<uint32_t>(wv >> 32);
+        e.pad = 0;
+        e.res = ~uint64_t(0);
+        myq[rank[q]] = e;
       }
-      qn += __popcll(bal);
+      na += __popcll(ba);
+      nb += __popcll(bb);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // finish the queued sub-vectors cooperatively
-    for (int qi = lane; qi < qn; qi += kWave) {
-      const QEntry e = myq[qi];
-      uint64_t best = ~uint64_t(0);
-      uint32_t ext = kExtBrute;
-      if (e.cell >= 0) ext = text[e.cell];
-      if (ext != kExtBrute && (ext >> 8) + (ext & 0xffu) > kPoolBytes) ext = kExtBrute;
-      if (ext == kExtBrute) {
-        for (int k = 0; k < kCodes; ++k) {
-          const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * k]);
+    if (na + nb > 0) {   // wave-uniform
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // A: one lane per entry, the four further candidates (ascending)
+      for (int qi = lane; qi < na; qi += kWave) {
+        const QEntry e = myq[qi];
+        uint64_t bk = ~uint64_t(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
+          const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
           const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-          const uint64_t key = dist_key(sqdist4(e.h, cv), static_cast<uint32_t>(k));
-          best = key < best ? key : best;
+          const uint64_t key = dist_key(sqdist4(e.h, cv), code);
+          bk = key < bk ? key : bk;
         }
-      } else {
-        const uint32_t o = ext >> 8, n = ext & 0xffu;
-        for (uint32_t i = 0; i < n; ++i) {
-          const uint32_t k = tpool[o + i];
-          const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * k]);
+        myq[qi].res = bk;
+      }
+      // B: the whole wave scans all codes of one entry at a time
+      for (int bi = 0; bi < nb; ++bi) {
+        const int qi = kQCap - 1 - bi;
+        const float4 hq = *reinterpret_cast<const float4*>(myq[qi].h);
+        const float hv[4] = {hq.x, hq.y, hq.z, hq.w};
+        uint64_t bk = ~uint64_t(0);
+#pragma unroll
+        for (int r = 0; r < kCodes / kWave; ++r) {
+          const uint32_t code = static_cast<uint32_t>(lane + kWave * r);
+          const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
           const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-          const uint64_t key = dist_key(sqdist4(e.h, cv), k);
-          best = key < best ? key : best;
+          const uint64_t key = dist_key(sqdist4(hv, cv), code);
+          bk = key < bk ? key : bk;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const uint64_t other = __shfl_xor(bk, o, kWave);
+          bk = other < bk ? other : bk;
+        }
+        if (lane == 0) myq[qi].res = bk;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (rank[q] >= 0) {
+          const uint64_t r = myq[rank[q]].res;
+          const float rd = __uint_as_float(static_cast<uint32_t>(r >> 32));
+          const uint32_t rc = static_cast<uint32_t>(r) & 0xffu;
+          const uint32_t oc = (codes4[mb] >> (8 * q)) & 0xffu;
+          const float od = bestd[4 * mb + q];
+          if (rd < od || (rd == od && rc < oc)) {
+            bestd[4 * mb + q] = rd;
+            codes4[mb] = (codes4[mb] & ~(0xffu << (8 * q))) | (rc << (8 * q));
+          }
         }
       }
-      atomicMin(reinterpret_cast<unsigned long long*>(&myres[e.slot]),
-                static_cast<unsigned long long>(best));
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   // ---- scale adjustment, codes, metadata
   float dot = 0.f, hh = 0.f;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int k = 0; k < 16; ++k) {
+    const int mb = k >> 2, q = k & 3;
+    const uint32_t code = (codes4[mb] >> (8 * q)) & 0xffu;
+    const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
+    const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t k = static_cast<uint32_t>(myres[(8 * mb + 2 * q + hf) * 32 + t]) & 0xffu;
-      const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * k]);
-      const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dot = fmaf(acc[mb][4 * q + e], cv[e], dot);
-        hh = fmaf(acc[mb][4 * q + e], acc[mb][4 * q + e], hh);
-      }
+    for (int e = 0; e < 4; ++e) {
+      dot = fmaf(acc[mb][4 * q + e], cv[e], dot);
+      hh = fmaf(acc[mb][4 * q + e], acc[mb][4 * q + e], hh);
     }
+  }
   dot += __shfl_xor(dot, 32, kWave);
   hh += __shfl_xor(hh, 32, kWave);
   const float alpha = (scale_adjust && dot > 0.f) ? hh / dot : 1.0f;
+  const uint32_t own[4] = {codes4[0], codes4[1], codes4[2], codes4[3]};
 
+  // Lane half 0 holds the even sub-vectors, half 1 the odd ones.  After the
+  // swap, half 0 has (own even, partner odd) codes of sub-vectors 0..15 and
+  // half 1 (partner even, own odd) of 16..31: interleave bytes and store.
+  uint32_t lo01[2] = {own[0], own[1]}, hi23[2] = {own[2], own[3]};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(lo01[i], hi23[i], false, false);
+    lo01[i] = r[0];
+    hi23[i] = r[1];
+  }
+  // half 0: even = lo01 (own), odd = hi23 (partner's codes 0..15)
+  // half 1: even = lo01 (partner's 16..31), odd = hi23 (own)
   uint32_t pk[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      v |= (static_cast<uint32_t>(myres[(16 * hf + 4 * i + b) * 32 + t]) & 0xffu) << (8 * b);
-    pk[i] = v;
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t ev = lo01[d >> 1], od = hi23[d >> 1];
+    pk[d] = __builtin_amdgcn_perm(od, ev, (d & 1) ? 0x07030602u : 0x05010400u);
   }
   *reinterpret_cast<u32x4*>(codes + seq * codes_seq_stride + tok * 32 + 16 * hf) =
       u32x4{pk[0], pk[1], pk[2], pk[3]};

@@ -16,10 +16,10 @@
 // of any point of the box -- including every lowest-index tie -- is always
 // in its list.  Points outside the grid take a full scan.
 //
-// Per box: u32 "main" = four codes.  With at most four candidates they are
-// ascending, padded by repeating the last; with more, the four lowest are
-// stored descending (main byte 0 > byte 1 flags the overflow) and the rest
-// sit in a byte pool, located by the u32 "ext" entry.
+// Per box: one u64 of eight candidate codes (encoding in nsn_device.h):
+// up to four ascending; five to eight split in two halves whose byte order
+// flags the overflow; more than eight (rare, far tails) tells the search to
+// scan all codes.
 #include <cmath>
 
 #include "nsn_device.h"
@@ -103,54 +103,6 @@ __device__ void load_codebook64(const uint8_t* table, double (*cw)[4], double* n
   n2[t] = s;
 }
 
-__global__ __launch_bounds__(256) void tab_count_kernel(uint8_t* __restrict__ table) {
-  __shared__ double cw[kCodes][4];
-  __shared__ double n2[kCodes];
-  __shared__ int cnt;
-  const int cell = blockIdx.x;
-  load_codebook64(table, cw, n2);
-  if (threadIdx.x == 0) cnt = 0;
-  __syncthreads();
-  double lo[4], hi[4];
-  box_of(cell, reinterpret_cast<const float*>(table + kTabEdges), lo, hi);
-  const bool a = alive_in_box(cw, n2, threadIdx.x, lo, hi);
-  if (a) atomicAdd(&cnt, 1);
-  __syncthreads();
-  if (threadIdx.x == 0) reinterpret_cast<uint32_t*>(table + kTabExt)[cell] = static_cast<uint32_t>(cnt);
-}
-
-// Exclusive scan of the extra counts (count - 4) in cell order; one block.
-__global__ __launch_bounds__(1024) void tab_scan_kernel(uint8_t* __restrict__ table) {
-  __shared__ uint32_t part[1024];
-  uint32_t* ext = reinterpret_cast<uint32_t*>(table + kTabExt);
-  const int t = threadIdx.x;
-  const int per = (kCells + 1023) / 1024;
-  const int a = t * per, b = min(kCells, a + per);
-  uint32_t s = 0;
-  for (int i = a; i < b; ++i) s += ext[i] > 4 ? ext[i] - 4 : 0;
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const uint32_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  uint32_t run = part[t] - s;  // exclusive prefix of this thread's range
-  for (int i = a; i < b; ++i) {
-    const uint32_t c = ext[i];
-    const uint32_t extra = c > 4 ? c - 4 : 0;
-    if (extra == 0) {
-      ext[i] = 0;
-    } else if (run + extra <= kPoolBytes && extra < 256) {
-      ext[i] = (run << 8) | extra;
-    } else {
-      ext[i] = kExtBrute;
-    }
-    run += extra;
-  }
-}
-
 __global__ __launch_bounds__(256) void tab_write_kernel(uint8_t* __restrict__ table) {
   __shared__ double cw[kCodes][4];
   __shared__ double n2[kCodes];
@@ -173,18 +125,22 @@ __global__ __launch_bounds__(256) void tab_write_kernel(uint8_t* __restrict__ ta
   __syncthreads();
   if (t == 0) {
     const uint32_t n = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-    uint32_t main = 0;
+    uint64_t w = 0;
     if (n <= 4) {
-      for (int i = 0; i < 4; ++i) main |= static_cast<uint32_t>(list[min<uint32_t>(i, n - 1)]) << (8 * i);
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t c = list[min<uint32_t>(i, n - 1)];
+        w |= c << (8 * i);
+        w |= c << (8 * (i + 4));
+      }
     } else {
-      for (int i = 0; i < 4; ++i) main |= static_cast<uint32_t>(list[3 - i]) << (8 * i);
+      for (int i = 0; i < 4; ++i) w |= static_cast<uint64_t>(list[3 - i]) << (8 * i);
+      if (n <= 8) {
+        for (int i = 0; i < 4; ++i) w |= static_cast<uint64_t>(list[min<uint32_t>(4 + i, n - 1)]) << (8 * (i + 4));
+      } else {
+        for (int i = 0; i < 4; ++i) w |= static_cast<uint64_t>(list[7 - i]) << (8 * (i + 4));
+      }
     }
-    reinterpret_cast<uint32_t*>(table + kTabMain)[cell] = main;
-  }
-  const uint32_t ext = reinterpret_cast<const uint32_t*>(table + kTabExt)[cell];
-  if (ext != 0 && ext != kExtBrute) {
-    const uint32_t off = ext >> 8, extra = ext & 0xffu;
-    if (static_cast<uint32_t>(t) < extra) table[kTabPool + off + t] = list[4 + t];
+    reinterpret_cast<uint64_t*>(table + kTabMain)[cell] = w;
   }
 }
 
@@ -225,16 +181,12 @@ __global__ __launch_bounds__(256) void nearest_kernel(const uint8_t* __restrict_
     }
     cell = min(cell, kCells - 1);   // in bounds even for an unprepared table
     if (!off) {
-      const uint32_t mainv = reinterpret_cast<const uint32_t*>(table + kTabMain)[cell];
-      for (int i = 0; i < 4; ++i) eval((mainv >> (8 * i)) & 0xffu);
-      brute = false;
-      if ((mainv & 0xffu) > ((mainv >> 8) & 0xffu)) {
-        const uint32_t ext = reinterpret_cast<const uint32_t*>(table + kTabExt)[cell];
-        if (ext == kExtBrute || (ext >> 8) + (ext & 0xffu) > kPoolBytes) {
-          brute = true;
-        } else {
-          for (uint32_t i = 0; i < (ext & 0xffu); ++i) eval(table[kTabPool + (ext >> 8) + i]);
-        }
+      const uint64_t wv = reinterpret_cast<const uint64_t*>(table + kTabMain)[cell];
+      brute = cand_more_than_8(wv);
+      if (!brute) {
+        for (int i = 0; i < 4; ++i) eval(static_cast<uint32_t>(wv >> (8 * i)) & 0xffu);
+        if (cand_more_than_4(wv))
+          for (int i = 4; i < 8; ++i) eval(static_cast<uint32_t>(wv >> (8 * i)) & 0xffu);
       }
     }
   }
@@ -260,8 +212,6 @@ hipError_t launch_search_table(void* table, hipStream_t s) {
   uint8_t* t = static_cast<uint8_t*>(table);
   const Edges E = make_edges();
   hipLaunchKernelGGL(tab_init_kernel, dim3((kFine + 255) / 256), dim3(256), 0, s, E, t);
-  hipLaunchKernelGGL(tab_count_kernel, dim3(kCells), dim3(256), 0, s, t);
-  hipLaunchKernelGGL(tab_scan_kernel, dim3(1), dim3(1024), 0, s, t);
   hipLaunchKernelGGL(tab_write_kernel, dim3(kCells), dim3(256), 0, s, t);
   return hipGetLastError();
 }
