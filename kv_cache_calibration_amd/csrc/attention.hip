@@ -35,7 +35,7 @@ namespace nsn {
 
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kHB = 4;              // query heads per workgroup
 constexpr int kMaxChunk = 8192;     // quantized tokens per workgroup, at most
@@ -71,24 +71,101 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Global data one wave needs for one 64-token tile, loaded one tile ahead.
+struct TileData {
+  u32x4 kc[2][2];   // score phase: this lane's token codes, blocks 0 and 1
+  uint32_t km, vm;  // metadata of token t0 + lane
+  uint32_t vc[8];   // value phase: unit u of tokens slot + 8 i
+  u32x4 osh;        // 8 fp16 of the group's V shift for the shift term
+};
+
+template <int M>
+__device__ __forceinline__ void load_tile(TileData& d, int t0, int c1, int lane, int u, int slot,
+                                          int sh_c, const uint8_t* kcrow, const uint8_t* vcrow,
+                                          const uint32_t* kmrow, const uint32_t* vmrow,
+                                          const uint16_t* vs_g) {
+  constexpr int CODE_BYTES = kD / M;
+  const int t32 = lane & 31;
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const int tt = t0 + 32 * bk + t32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) d.kc[bk][i] = u32x4{0u, 0u, 0u, 0u};
+    if (tt < c1) {
+      const uint8_t* src = kcrow + static_cast<int64_t>(tt) * CODE_BYTES;
+#pragma unroll
+      for (int i = 0; i < CODE_BYTES / 16; ++i) d.kc[bk][i] = load_nt16(src + 16 * i);
+    }
+  }
+  const int t = t0 + lane;
+  d.km = t < c1 ? __builtin_nontemporal_load(kmrow + t) : 0u;
+  d.vm = t < c1 ? __builtin_nontemporal_load(vmrow + t) : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tv = t0 + slot + 8 * i;
+    uint32_t v = 0;
+    if (tv < c1) {
+      if constexpr (M == 4)
+        v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcrow + static_cast<int64_t>(tv) * CODE_BYTES) + u);
+      else
+        v = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(vcrow + static_cast<int64_t>(tv) * CODE_BYTES) + u);
+    }
+    d.vc[i] = v;
+  }
+  d.osh = load_nt16(vs_g + sh_c);
+}
+
+// One 16-channel MFMA step of the scores, for compile-time step ST (keeps
+// every register index constant), then the next step.
+template <int M, int ST>
+__device__ __forceinline__ void score_steps(v16f& sc, const u32x4 (&qa)[8], const uint32_t (&w8)[8],
+                                            int hf, const uint32_t* cbh) {
+  if constexpr (ST < 8) {
+    u32x4 bv;
+    if constexpr (M == 4) {
+      // sub-vectors 4 ST + 2 hf and + 1: bytes 2 hf, 2 hf + 1 of code word ST
+      const uint32_t wd = w8[ST];
+      const uint32_t ca = (wd >> (16 * hf)) & 0xffu;
+      const uint32_t cb2 = (wd >> (16 * hf + 8)) & 0xffu;
+      const uint2 xa = *reinterpret_cast<const uint2*>(&cbh[ca * 2]);
+      const uint2 xb = *reinterpret_cast<const uint2*>(&cbh[cb2 * 2]);
+      bv = u32x4{xa.x, xa.y, xb.x, xb.y};
+    } else {
+      // sub-vector 2 ST + hf: byte (2 ST + hf) & 3 of code word (2 ST + hf) / 4
+      const uint32_t wd = w8[ST >> 1];
+      const uint32_t ca = (wd >> (8 * (((2 * ST) & 3) + hf))) & 0xffu;
+      const uint4 xa = *reinterpret_cast<const uint4*>(&cbh[ca * 4]);
+      bv = u32x4{xa.x, xa.y, xa.z, xa.w};
+    }
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, qa[ST]),
+                                                 __builtin_bit_cast(v8h, bv), sc, 0, 0, 0);
+    score_steps<M, ST + 1>(sc, qa, w8, hf, cbh);
+  }
+}
+
 template <int M, int G>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(SplitParams p) {
   constexpr int NSUB = kD / M;
   constexpr int CODE_BYTES = NSUB;   // bytes of codes per token
   constexpr int UPOS = 16 / M;       // sub-vector positions per 16-channel unit
   constexpr int CW = M / 2;          // dwords per fp16 codeword
   constexpr int kMaxGroups = kMaxChunk / G;
 
-  __shared__ float4 lut[NSUB * kCodes];   // T[j][code] -> 4 heads (also the merge scratch)
-  __shared__ uint32_t cbh[kCodes * CW];   // fp16 codebook, CW dwords per code
+  __shared__ __attribute__((aligned(16))) uint32_t cbh[kCodes * CW];   // fp16 codebook
   __shared__ float qr[kHB][kD];
   __shared__ float qo[kMaxGroups][kHB];
   __shared__ uint2 wbuf[kWaves][64];      // per-wave fp16 weights of the tile's tokens
-  __shared__ float wm[kWaves][kHB];       // per-wave running max, for the merge
+  __shared__ float wm[kWaves][kHB];
+  __shared__ float wl[kWaves][kHB];
+  __shared__ float wacc[kWaves][kHB][kD];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const int t32 = lane & 31, hf = lane >> 5;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y / p.hblocks;
   const int hb = blockIdx.y - kvh * p.hblocks;
@@ -99,26 +176,26 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
   const int c1 = min(p.n_quant, c0 + p.chunk);
   const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;  // (b, kvh) cache row
 
-  // ---- set-up: fp16 codebook, rotated queries, per-group <q', o'_g>, table
+  // ---- set-up: fp16 codebook, rotated queries, per-group <q', o'_g>
   const uint32_t* cbg = reinterpret_cast<const uint32_t*>(p.table + kTabCodebookH);
   for (int i = tid; i < kCodes * CW; i += kThreads) cbh[i] = cbg[i];
-  if (tid < kHB * kD) {
-    const int h = tid / kD, c = tid % kD;
+  for (int i = tid; i < kHB * kD; i += kThreads) {
+    const int h = i / kD, c = i % kD;
     qr[h][c] = h < nh ? h2f(p.q[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c]) : 0.f;
   }
   __syncthreads();
 #pragma unroll 1
   for (int st = 1; st < kD; st <<= 1) {
-    if (tid < kHB * kD / 2) {
-      const int h = tid / (kD / 2), pr = tid % (kD / 2);
-      const int i = ((pr / st) * 2 * st) + (pr % st);
-      const float a = qr[h][i], bb = qr[h][i + st];
-      qr[h][i] = a + bb;
-      qr[h][i + st] = a - bb;
+    for (int i = tid; i < kHB * kD / 2; i += kThreads) {
+      const int h = i / (kD / 2), pr = i % (kD / 2);
+      const int k = ((pr / st) * 2 * st) + (pr % st);
+      const float a = qr[h][k], bb = qr[h][k + st];
+      qr[h][k] = a + bb;
+      qr[h][k + st] = a - bb;
     }
     __syncthreads();
   }
-  if (tid < kHB * kD) qr[tid / kD][tid % kD] *= kInvSqrtD;
+  for (int i = tid; i < kHB * kD; i += kThreads) qr[i / kD][i % kD] *= kInvSqrtD;
   __syncthreads();
 
   const int ng = (c1 - c0) / G;
@@ -130,22 +207,30 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
     s = wave_sum(s);
     if (lane == 0) qo[g][h] = s;
   }
+  // MFMA A operand, one per 16-channel step: rows 0..3 = fp16(q'_h),
+  // rows 8..11 = fp16(q'_h - fp16(q'_h)) (so the pair carries ~22 bits), other
+  // rows zero; lane (row t32, channels 16 s + 8 hf .. + 7)
+  u32x4 qa[8];
   {
-    const float* cbf = reinterpret_cast<const float*>(p.table + kTabCodebook);
-    for (int e = tid; e < NSUB * kCodes; e += kThreads) {
-      const int j = e / kCodes, k = e % kCodes;
-      float c[M];
+    const bool is_hi = t32 < kHB, is_lo = t32 >= 8 && t32 < 8 + kHB;
+    const int hq = is_hi ? t32 : (is_lo ? t32 - 8 : 0);
 #pragma unroll
-      for (int i = 0; i < M; ++i) c[i] = cbf[k * M + i];
-      float t[kHB];
+    for (int st = 0; st < 8; ++st) {
+      uint32_t wv[4];
 #pragma unroll
-      for (int h = 0; h < kHB; ++h) {
-        float s = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        uint32_t pk = 0;
 #pragma unroll
-        for (int i = 0; i < M; ++i) s = fmaf(qr[h][M * j + i], c[i], s);
-        t[h] = s;
+        for (int e = 0; e < 2; ++e) {
+          const float v = qr[hq][16 * st + 8 * hf + 2 * i + e];
+          const uint16_t hi = f2h(v);
+          const uint16_t lo = f2h(v - h2f(hi));
+          const uint16_t val = is_hi ? hi : (is_lo ? lo : 0);
+          pk |= static_cast<uint32_t>(val) << (16 * e);
+        }
+        wv[i] = pk;
       }
-      lut[e] = make_float4(t[0], t[1], t[2], t[3]);
+      qa[st] = u32x4{wv[0], wv[1], wv[2], wv[3]};
     }
   }
   __syncthreads();
@@ -174,54 +259,56 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
   const uint32_t* vmrow = reinterpret_cast<const uint32_t*>(p.vm + row * p.cap * 2);
   const uint16_t* vsrow = p.vs + row * (p.cap / G) * kD;
 
+  TileData cur;
+  if (c0 + 64 * wave < c1)
+    load_tile<M>(cur, c0 + 64 * wave, c1, lane, u, slot, sh_c, kcrow, vcrow, kmrow, vmrow,
+                 vsrow + static_cast<int64_t>((c0 + 64 * wave) / G) * kD);
   for (int t0 = c0 + 64 * wave; t0 < c1; t0 += 64 * kWaves) {
-    // -- score phase: lane = token
+    TileData nxt;
+    const int tn = t0 + 64 * kWaves;
+    if (tn < c1)
+      load_tile<M>(nxt, tn, c1, lane, u, slot, sh_c, kcrow, vcrow, kmrow, vmrow,
+                   vsrow + static_cast<int64_t>(tn / G) * kD);
+    // -- scores on MFMA: block bk covers tokens t0 + 32 bk + t32
+    float sblk[2][kHB];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      uint32_t w8[8];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        w8[4 * i] = cur.kc[bk][i].x;
+        w8[4 * i + 1] = cur.kc[bk][i].y;
+        w8[4 * i + 2] = cur.kc[bk][i].z;
+        w8[4 * i + 3] = cur.kc[bk][i].w;
+      }
+      v16f sc = v16f{};
+      score_steps<M, 0>(sc, qa, w8, hf, cbh);
+#pragma unroll
+      for (int h = 0; h < kHB; ++h) sblk[bk][h] = sc[h] + sc[4 + h];   // hi + lo rows (lanes < 32)
+    }
+    // lanes 32..63 take block 1's tokens: lane l now holds token t0 + l
+    float dotq[kHB];
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sblk[0][h]),
+                                                      __float_as_uint(sblk[1][h]), false, false);
+      dotq[h] = __uint_as_float(r[0]);
+    }
     const int t = t0 + lane;
     const bool valid = t < c1;
-    uint32_t w8[8];
-    uint32_t kmv = 0, vmv = 0;
-    if (valid) {
-      const uint8_t* src = kcrow + static_cast<int64_t>(t) * CODE_BYTES;
-#pragma unroll
-      for (int i = 0; i < CODE_BYTES / 16; ++i) {
-        const u32x4 c = load_nt16(src + 16 * i);
-        w8[4 * i] = c.x;
-        w8[4 * i + 1] = c.y;
-        w8[4 * i + 2] = c.z;
-        w8[4 * i + 3] = c.w;
-      }
-      kmv = __builtin_nontemporal_load(kmrow + t);
-      vmv = __builtin_nontemporal_load(vmrow + t);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w8[i] = 0u;
-    }
-    float4 dot = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < NSUB; ++j) {
-      const uint32_t code = (w8[j >> 2] >> (8 * (j & 3))) & 0xffu;
-      const float4 L = lut[j * kCodes + code];
-      dot.x += L.x;
-      dot.y += L.y;
-      dot.z += L.z;
-      dot.w += L.w;
-      // keep at most 8 table reads in flight (register pressure)
-      if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-    }
+    const uint32_t kmv = cur.km, vmv = cur.vm;
     const int g = (t0 - c0) / G;  // one group per tile (64 divides G)
     const float s1k = h2f(kmv & 0xffffu), s2k = h2f(kmv >> 16);
     const float s1v = h2f(vmv & 0xffffu), s2v = h2f(vmv >> 16);
     const float ks1 = p.scale * s1k;
     float s[kHB];
-    s[0] = ks1 * fmaf(s2k, dot.x, qo[g][0]);
-    s[1] = ks1 * fmaf(s2k, dot.y, qo[g][1]);
-    s[2] = ks1 * fmaf(s2k, dot.z, qo[g][2]);
-    s[3] = ks1 * fmaf(s2k, dot.w, qo[g][3]);
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) s[h] = ks1 * fmaf(s2k, dotq[h], qo[g][h]);
     float pw[kHB], gs[kHB];
 #pragma unroll
     for (int h = 0; h < kHB; ++h) {
       if (!valid) s[h] = -__builtin_huge_valf();
-      const float mnew = fmaxf(m_run[h], wave_max(s[h]));  // wave-uniform
+      const float mnew = fmaxf(m_run[h], wave_max_fast(s[h]));  // wave-uniform
       if (mnew > m_run[h]) {
         const float f = __expf(m_run[h] - mnew);
         m_run[h] = mnew;
@@ -235,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
       }
       pw[h] = valid ? __expf(s[h] - m_run[h]) : 0.f;
       l_lane[h] += pw[h];
-      gs[h] = wave_sum(pw[h] * s1v);
+      gs[h] = wave_sum_fast(pw[h] * s1v);
     }
     const float sv = s1v * s2v;
     wbuf[wave][lane] = make_uint2(
@@ -243,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
         static_cast<uint32_t>(f2h(pw[2] * sv)) | (static_cast<uint32_t>(f2h(pw[3] * sv)) << 16));
     // shift term p s1 o'_g: this lane owns head sh_h, channels sh_c .. sh_c + 7
     {
-      const u32x4 o = load_nt16(vsrow + static_cast<int64_t>(c0 / G + g) * kD + sh_c);
+      const u32x4 o = cur.osh;
       const float gsh = sh_h == 0 ? gs[0] : sh_h == 1 ? gs[1] : sh_h == 2 ? gs[2] : gs[3];
       const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
@@ -257,18 +344,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // -- value phase: lane = (unit u, slot); token pairs (a, a + 8)
-#pragma unroll 2
+#pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int ia = slot + 16 * k, ib = ia + 8;
-      const int ta = t0 + ia, tb = t0 + ib;
-      uint32_t va = 0, vb = 0;
-      if constexpr (M == 4) {
-        if (ta < c1) va = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcrow + static_cast<int64_t>(ta) * CODE_BYTES) + u);
-        if (tb < c1) vb = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcrow + static_cast<int64_t>(tb) * CODE_BYTES) + u);
-      } else {
-        if (ta < c1) va = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(vcrow + static_cast<int64_t>(ta) * CODE_BYTES) + u);
-        if (tb < c1) vb = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(vcrow + static_cast<int64_t>(tb) * CODE_BYTES) + u);
-      }
+      const uint32_t va = cur.vc[2 * k], vb = cur.vc[2 * k + 1];
       const uint2 wa = wbuf[wave][ia], wb = wbuf[wave][ib];
       const uint32_t wp[kHB] = {pair_lo(wa.x, wb.x), pair_hi(wa.x, wb.x), pair_lo(wa.y, wb.y),
                                 pair_hi(wa.y, wb.y)};
@@ -295,9 +374,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    cur = nxt;
   }
 
-  // ---- merge: slots inside each wave, then the 16 waves
+  // ---- merge: slots inside each wave, then the waves
 #pragma unroll
   for (int h = 0; h < kHB; ++h) {
     l_lane[h] = wave_sum(l_lane[h]);
@@ -310,30 +390,29 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
       acc[h][i] = v;
     }
   }
-  __syncthreads();  // every wave is done with the lookup table
-  float* wacc = reinterpret_cast<float*>(lut);        // [kWaves][4][128]
-  float* wl = wacc + kWaves * kHB * kD;               // [kWaves][4]
   if (slot == 0) {
 #pragma unroll
     for (int h = 0; h < kHB; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) wacc[(wave * kHB + h) * kD + 16 * u + i] = acc[h][i];
+      for (int i = 0; i < 16; ++i) wacc[wave][h][16 * u + i] = acc[h][i];
   }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < kHB; ++h) {
       wm[wave][h] = m_run[h];
-      wl[wave * kHB + h] = l_lane[h];
+      wl[wave][h] = l_lane[h];
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // the shift-term accumulators: each (head, channel) of a wave's row has
   // exactly one owner lane, so a plain read-modify-write is race free
 #pragma unroll
-  for (int i = 0; i < 8; ++i) wacc[(wave * kHB + sh_h) * kD + sh_c + i] += sh[i];
+  for (int i = 0; i < 8; ++i) wacc[wave][sh_h][sh_c + i] += sh[i];
   __syncthreads();
-  if (tid < kHB * kD) {
-    const int h = tid / kD, c = tid % kD;
+  for (int idx = tid; idx < kHB * kD; idx += kThreads) {
+    const int h = idx / kD, c = idx % kD;
     float M_ = -__builtin_huge_valf();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, wm[w][h]);
@@ -341,8 +420,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(SplitParams p) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float e = wm[w][h] == -__builtin_huge_valf() ? 0.f : __expf(wm[w][h] - M_);
-      a = fmaf(e, wacc[(w * kHB + h) * kD + c], a);
-      l = fmaf(e, wl[w * kHB + h], l);
+      a = fmaf(e, wacc[w][h][c], a);
+      l = fmaf(e, wl[w][h], l);
     }
     if (h < nh) {
       float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * p.n_split + split) * kPartStride;
@@ -509,7 +588,7 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int* n_split
   const int grp = Hq / Hkv;
   const int64_t units = static_cast<int64_t>(B) * Hkv * ((grp + kHB - 1) / kHB);
   const int max_split = (n_quant + kMinChunk - 1) / kMinChunk;
-  int64_t want = (1024 + units - 1) / units;  // about four workgroups per CU
+  int64_t want = (3072 + units - 1) / units;  // about four rounds of three workgroups per CU
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   int64_t c = (n_quant + want - 1) / want;

@@ -5,6 +5,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nsn {
 
 constexpr int kD = 128;      // head_dim
@@ -87,6 +89,42 @@ __device__ __forceinline__ void fwht_regs(float (&v)[N]) {
       }
     }
   }
+}
+
+// Wave-wide all-reduce on the VALU: DPP within rows of 16 lanes (xor 1,
+// xor 2, rotate 4, rotate 8), then gfx950 permlane swaps across the row pairs
+// and the two halves.  Every lane ends with the full result.
+template <typename Op>
+__device__ __forceinline__ float wave_allreduce_dpp(float x, Op op) {
+  auto dpp = [](float v, auto ctrl_c) {
+    constexpr int ctrl = decltype(ctrl_c)::value;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false));
+  };
+  x = op(x, dpp(x, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  x = op(x, dpp(x, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  x = op(x, dpp(x, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  x = op(x, dpp(x, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return x;
+}
+__device__ __forceinline__ float wave_sum_fast(float x) {
+  return wave_allreduce_dpp(x, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ float wave_max_fast(float x) {
+  return wave_allreduce_dpp(x, [](float a, float b) { return fmaxf(a, b); });
+}
+// x(lane) + x(lane ^ 32) on the VALU (permlane32 swap of x with itself
+// yields the lower half in one result and the upper half in the other).
+__device__ __forceinline__ float half_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) ss = fmaf(acc[mb][r], acc[mb][r], ss);
-  ss += __shfl_xor(ss, 32, kWave);
+  ss = half_pair_sum(ss);
   const float nrm = sqrtf(ss);
   const float s1 = nrm * (1.0f / kD);
   const float a_t = nrm > 0.f ? kSqrtD / nrm : 0.f;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       float s = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s = fmaf(av[r], c2[r], s);
-      s += __shfl_xor(s, 32, kWave);
+      s = half_pair_sum(s);
       if (hf == 0) csum[w][32 * nb + t] = s;
     }
   }
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
         ss2 = fmaf(z, z, ss2);
       }
     }
-  ss2 += __shfl_xor(ss2, 32, kWave);
+  ss2 = half_pair_sum(ss2);
   const float s2 = sqrtf(ss2 * (1.0f / kD));
   const float inv2 = s2 > 0.f ? 1.0f / s2 : 0.f;
 #pragma unroll
@@ -340,8 +340,8 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       hh = fmaf(acc[mb][4 * q + e], acc[mb][4 * q + e], hh);
     }
   }
-  dot += __shfl_xor(dot, 32, kWave);
-  hh += __shfl_xor(hh, 32, kWave);
+  dot = half_pair_sum(dot);
+  hh = half_pair_sum(hh);
   const float alpha = (scale_adjust && dot > 0.f) ? hh / dot : 1.0f;
   const uint32_t own[4] = {codes4[0], codes4[1], codes4[2], codes4[3]};
 
