@@ -4,30 +4,35 @@
 //  cache into a quantized part and a full-precision residual; the attention
 //  score takes the NSN byproducts s1, s2, o directly.]
 //
-// Everything on quantized tokens happens in the rotated domain: with
-// q' = H q / sqrt(d) (computed once per workgroup),
+// Quantized tokens are handled in the rotated domain.  With q' = H q / sqrt(d),
 //   <q, x_hat_t> = s1_t (s2'_t <q', c(codes_t)> + <q', o'_g>),
-// so a key is never dequantized.  <q', c(codes_t)> is a sum over the token's
-// sub-vectors of a per-workgroup lookup table
-//   T[j][code] = ( <q'_h[m j : m j + m], C[code]> )_{h < 4}
-// (one 16-byte LDS read gives all four heads).  Values are accumulated in the
-// rotated domain and rotated back once per query head in the combine kernel.
+// so keys are never dequantized, and the rotated value sum splits into
+//   sum_t p_t s1_t s2'_t c(codes_t)  +  sum_g o'_g sum_{t in g} p_t s1_t;
+// one inverse rotation per query head at the end gives the output.
 //
-// attn_split_kernel: one workgroup (16 waves) per (token chunk, kv head,
-//   block of up to 4 query heads, batch).  After the shared set-up (rotated
-//   queries, per-group <q', o'_g>, lookup table) every wave runs its own
-//   online softmax over 64-token tiles with no workgroup barrier:
-//     score phase  lane = token: table lookups, scale, wave max, exp;
-//                  weights w = p s1 s2' go to a per-wave LDS buffer (fp16);
-//     value phase  lane = (16-channel unit, token slot): tokens are taken in
-//                  pairs so one v_dot2_f32_f16 does w_a c_a + w_b c_b into an
-//                  fp32 accumulator (codewords are exact fp16 values);
-//     shift term   p s1 o'_g, from the wave-summed p s1 of the tile.
-//   The 16 wave partials are merged through LDS at the end and one
-//   (acc[128], max, sum) partial per head is written.
-// attn_combine_kernel: one workgroup per (kv head block, batch): the
-//   residual window's exact fp16 attention, a log-sum-exp merge with the
-//   chunk partials, one inverse rotation, normalization.
+// attn_split_kernel: one workgroup (4 waves) per (token chunk, kv head, block
+//   of up to 4 query heads, batch).  Tile i (64 tokens) of the chunk belongs
+//   to wave i mod 4; each wave runs its own online softmax with no workgroup
+//   barrier:
+//     scores   16 MFMA 16x16x32 (fp16 in, fp32 out): rows = the 4 heads' q'
+//              split into an fp16 high and low part, columns = 16 tokens,
+//              K = 32 channels; the B operand is two fp16 codewords per lane
+//              read straight from the codebook in LDS.  Two permlane swaps
+//              leave lane l with token l's 4 scores.
+//     softmax  base-2 exponent; the running max is raised (and the
+//              accumulators rescaled) only when some score exceeds it.
+//     values   16 MFMA: A = codewords, transposed on the fly by
+//              ds_read_b64_tr_b16 from the codebook (the lanes' addresses
+//              select the codes), B = the tile's fp16 high/low weights
+//              p s1 s2' from a per-wave LDS row buffer.
+//     shift    the tile's sum of p s1 per head (fp32) is kept in LDS with the
+//              max it refers to and applied to the group shifts at the end.
+//   Workgroup index n_split along x handles the fp16 residual window instead
+//   (exact scores, original domain).
+// attn_combine_kernel: one wave per (batch, query head): log-sum-exp merge of
+//   the chunk partials, inverse rotation, residual partial, normalization.
+#include <type_traits>
+
 #include "nsn_device.h"
 #include "nsn_launch.h"
 
@@ -37,13 +42,24 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kHB = 4;              // query heads per workgroup
-constexpr int kMaxChunk = 8192;     // quantized tokens per workgroup, at most
-constexpr int kMinChunk = 1024;
-constexpr int kPartStride = 132;    // acc[128], m, l, pad
+constexpr int kHB = 4;               // query heads per workgroup
+constexpr int kTile = 64;            // tokens per wave iteration
+constexpr int kMaxChunk = 8192;      // quantized tokens per workgroup, at most
+constexpr int kMaxTiles = kMaxChunk / kTile;
+constexpr int kMaxGroups = kMaxChunk / 128;
+constexpr int kMinChunk = 512;
+constexpr int kMaxResid = 1024;
+constexpr int kPartStride = 132;     // acc[128], m, l, pad
+constexpr int kBlocksPerCU = 3;      // resident split workgroups per CU (VGPR bound)
+constexpr int kPlanCUs = 256;
 constexpr float kInvSqrtD = 0.08838834764831845f;
+constexpr float kLog2e = 1.4426950408889634f;
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 struct SplitParams {
   const uint16_t* q;
@@ -53,425 +69,171 @@ struct SplitParams {
   const uint16_t* vm;
   const uint16_t* ks;
   const uint16_t* vs;
+  const uint16_t* kr;
+  const uint16_t* vr;
   const uint8_t* table;
   float* work;
-  int Hq, Hkv, grp, hblocks, n_quant, n_split, chunk;
-  int64_t cap;
+  int Hq, Hkv, grp, hblocks, n_quant, n_split, chunk, n_resid;
+  int64_t cap, rcap;
   float scale;
 };
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
-}
-// (lo half of a, lo half of b) and (hi half of a, hi half of b)
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+struct SplitSmem {
+  uint32_t cbh[kCodes * 4];          // fp16 codebook: 8 (m = 4) or 16 (m = 8) bytes per code
+  float qr[kHB][kD];                 // rotated queries
+  float qo[kMaxGroups][kHB];         // <q'_h, o'_g> per group of the chunk
+  float sg[kMaxGroups][kHB];         // per group: sum of p s1, relative to the final max
+  float ssum[kMaxTiles][kHB];        // per tile: sum of p s1 ...
+  float smax[kMaxTiles][kHB];        // ... relative to this max
+  // per-wave weight rows [token][slot] (slots 0..3 fp16 high part of p s1 s2'
+  // of heads 0..3, 4..7 low part, 8..15 zero); after the tile loop the same
+  // 2 KB hold the wave's value sums as float[kHB][kD]
+  uint16_t wrow[kWaves][kTile][16];
+  float wm[kWaves][kHB];
+  float wl[kWaves][kHB];
+};
+struct ResidSmem {
+  float qf[kHB][kD];
+  float sres[kHB][kMaxResid];
+  float red[kWaves][kHB];
+};
+union AttnSmem {
+  SplitSmem s;
+  ResidSmem r;
+};
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane 4a + b receives
+// element b of the 8-byte chunks addressed by lanes 4k + a, k = 0..3.  With
+// chunk (lane 4k + a) = 4 channels of token k, lane 4a + b gets one channel
+// of 4 consecutive tokens: the k-major layout of an MFMA operand.
+__device__ __forceinline__ uint2 ds_tr16(uint32_t lds_byte_addr) {
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<lds_v4s*>(static_cast<uintptr_t>(lds_byte_addr)));
+  return __builtin_bit_cast(uint2, r);
 }
 
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
 
-// Global data one wave needs for one 64-token tile, loaded one tile ahead.
+// byte K of w, times 2^S (a byte offset into the codebook)
+template <int K, int S>
+__device__ __forceinline__ uint32_t code_off(uint32_t w) {
+  return ((w >> (8 * K)) & 0xffu) << S;
+}
+
+__device__ __forceinline__ v4f mfma16(const u32x4& a, const u32x4& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b),
+                                                c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int M>
 struct TileData {
-  u32x4 kc[2][2];   // score phase: this lane's token codes, blocks 0 and 1
-  uint32_t km, vm;  // metadata of token t0 + lane
-  uint32_t vc[8];   // value phase: unit u of tokens slot + 8 i
-  u32x4 osh;        // 8 fp16 of the group's V shift for the shift term
+  using CT = std::conditional_t<M == 4, u32x2, uint32_t>;
+  // key codes of token 16 tb + lane % 16: bytes 8R.. (m = 4) or 4R.. (m = 8)
+  // of the token, R = lane / 16
+  CT kc[4];
+  // value codes of token 32 (i / 2) + 8R + 4 (i % 2) + (lane % 16) / 4:
+  // bytes 8a.. (m = 4) or 4a.. (m = 8), a = lane % 4
+  CT vc[4];
+  uint32_t km, vm;  // (s1, s2') of token `lane`
 };
 
 template <int M>
-__device__ __forceinline__ void load_tile(TileData& d, int t0, int c1, int lane, int u, int slot,
-                                          int sh_c, const uint8_t* kcrow, const uint8_t* vcrow,
-                                          const uint32_t* kmrow, const uint32_t* vmrow,
-                                          const uint16_t* vs_g) {
-  constexpr int CODE_BYTES = kD / M;
-  const int t32 = lane & 31;
+__device__ __forceinline__ void load_tile(TileData<M>& d, const uint8_t* kb, const uint8_t* vb,
+                                          const uint32_t* kmb, const uint32_t* vmb, uint32_t koff,
+                                          uint32_t voff, int lane) {
+  constexpr int CB = kD / M;
+  using CT = typename TileData<M>::CT;
 #pragma unroll
-  for (int bk = 0; bk < 2; ++bk) {
-    const int tt = t0 + 32 * bk + t32;
+  for (int tb = 0; tb < 4; ++tb)
+    d.kc[tb] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(kb + koff + 16 * tb * CB));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) d.kc[bk][i] = u32x4{0u, 0u, 0u, 0u};
-    if (tt < c1) {
-      const uint8_t* src = kcrow + static_cast<int64_t>(tt) * CODE_BYTES;
-#pragma unroll
-      for (int i = 0; i < CODE_BYTES / 16; ++i) d.kc[bk][i] = load_nt16(src + 16 * i);
-    }
-  }
-  const int t = t0 + lane;
-  d.km = t < c1 ? __builtin_nontemporal_load(kmrow + t) : 0u;
-  d.vm = t < c1 ? __builtin_nontemporal_load(vmrow + t) : 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tv = t0 + slot + 8 * i;
-    uint32_t v = 0;
-    if (tv < c1) {
-      if constexpr (M == 4)
-        v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcrow + static_cast<int64_t>(tv) * CODE_BYTES) + u);
-      else
-        v = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(vcrow + static_cast<int64_t>(tv) * CODE_BYTES) + u);
-    }
-    d.vc[i] = v;
-  }
-  d.osh = load_nt16(vs_g + sh_c);
+  for (int i = 0; i < 4; ++i)
+    d.vc[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const CT*>(vb + voff + (32 * (i >> 1) + 4 * (i & 1)) * CB));
+  d.km = __builtin_nontemporal_load(kmb + lane);
+  d.vm = __builtin_nontemporal_load(vmb + lane);
 }
 
-// One 16-channel MFMA step of the scores, for compile-time step ST (keeps
-// every register index constant), then the next step.
-template <int M, int ST>
-__device__ __forceinline__ void score_steps(v16f& sc, const u32x4 (&qa)[8], const uint32_t (&w8)[8],
-                                            int hf, const uint32_t* cbh) {
-  if constexpr (ST < 8) {
-    u32x4 bv;
-    if constexpr (M == 4) {
-      // sub-vectors 4 ST + 2 hf and + 1: bytes 2 hf, 2 hf + 1 of code word ST
-      const uint32_t wd = w8[ST];
-      const uint32_t ca = (wd >> (16 * hf)) & 0xffu;
-      const uint32_t cb2 = (wd >> (16 * hf + 8)) & 0xffu;
-      const uint2 xa = *reinterpret_cast<const uint2*>(&cbh[ca * 2]);
-      const uint2 xb = *reinterpret_cast<const uint2*>(&cbh[cb2 * 2]);
-      bv = u32x4{xa.x, xa.y, xb.x, xb.y};
-    } else {
-      // sub-vector 2 ST + hf: byte (2 ST + hf) & 3 of code word (2 ST + hf) / 4
-      const uint32_t wd = w8[ST >> 1];
-      const uint32_t ca = (wd >> (8 * (((2 * ST) & 3) + hf))) & 0xffu;
-      const uint4 xa = *reinterpret_cast<const uint4*>(&cbh[ca * 4]);
-      bv = u32x4{xa.x, xa.y, xa.z, xa.w};
-    }
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, qa[ST]),
-                                                 __builtin_bit_cast(v8h, bv), sc, 0, 0, 0);
-    score_steps<M, ST + 1>(sc, qa, w8, hf, cbh);
+// Score B operand of step s for token block tb: the channels 32R + 8s .. + 7
+// (R = lane / 16) of the lane's token, i.e. sub-vectors 8R + 2s, 8R + 2s + 1
+// (m = 4) or 4R + s (m = 8).
+template <int M, int S>
+__device__ __forceinline__ u32x4 score_b(const typename TileData<M>::CT& kc, const uint32_t* cbh) {
+  const char* base = reinterpret_cast<const char*>(cbh);
+  if constexpr (M == 4) {
+    const uint32_t w = kc[S >> 1];
+    const u32x2 c0 = *reinterpret_cast<const u32x2*>(base + code_off<2 * (S & 1), 3>(w));
+    const u32x2 c1 = *reinterpret_cast<const u32x2*>(base + code_off<2 * (S & 1) + 1, 3>(w));
+    return u32x4{c0.x, c0.y, c1.x, c1.y};
+  } else {
+    return *reinterpret_cast<const u32x4*>(base + code_off<S, 4>(kc));
   }
 }
 
-template <int M, int G>
-__global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(SplitParams p) {
-  constexpr int NSUB = kD / M;
-  constexpr int CODE_BYTES = NSUB;   // bytes of codes per token
-  constexpr int UPOS = 16 / M;       // sub-vector positions per 16-channel unit
-  constexpr int CW = M / 2;          // dwords per fp16 codeword
-  constexpr int kMaxGroups = kMaxChunk / G;
+// Value A operand chunk of channel block CB for one token: channels
+// 4 (8a + CB) .. + 3 (a = lane % 4): code byte CB (m = 4) or half CB % 2 of
+// code byte CB / 2 (m = 8) of the lane's value-code bytes.
+template <int M, int CB>
+__device__ __forceinline__ uint32_t value_chunk_off(const typename TileData<M>::CT& vc) {
+  if constexpr (M == 4)
+    return code_off<CB & 3, 3>(vc[CB >> 2]);
+  else
+    return code_off<(CB >> 1), 4>(vc) + 8u * (CB & 1);
+}
 
-  __shared__ __attribute__((aligned(16))) uint32_t cbh[kCodes * CW];   // fp16 codebook
-  __shared__ float qr[kHB][kD];
-  __shared__ float qo[kMaxGroups][kHB];
-  __shared__ uint2 wbuf[kWaves][64];      // per-wave fp16 weights of the tile's tokens
-  __shared__ float wm[kWaves][kHB];
-  __shared__ float wl[kWaves][kHB];
-  __shared__ float wacc[kWaves][kHB][kD];
+template <int M, int CB>
+__device__ __forceinline__ void value_steps(v4f (&acc)[8], const TileData<M>& d, int kb, const u32x4& bw,
+                                            uint32_t cbh_base) {
+  if constexpr (CB < 8) {
+    const uint2 a0 = ds_tr16(cbh_base + value_chunk_off<M, CB>(d.vc[2 * kb]));
+    const uint2 a1 = ds_tr16(cbh_base + value_chunk_off<M, CB>(d.vc[2 * kb + 1]));
+    acc[CB] = mfma16(u32x4{a0.x, a0.y, a1.x, a1.y}, bw, acc[CB]);
+    value_steps<M, CB + 1>(acc, d, kb, bw, cbh_base);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int t32 = lane & 31, hf = lane >> 5;
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / p.hblocks;
-  const int hb = blockIdx.y - kvh * p.hblocks;
-  const int b = blockIdx.z;
-  const int h0 = kvh * p.grp + hb * kHB;
-  const int nh = min(kHB, p.grp - hb * kHB);
-  const int c0 = split * p.chunk;
-  const int c1 = min(p.n_quant, c0 + p.chunk);
-  const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;  // (b, kvh) cache row
+template <int M, int S>
+__device__ __forceinline__ void score_steps(v4f& sa, const u32x4 (&qa)[4], const typename TileData<M>::CT& kc,
+                                            const uint32_t* cbh) {
+  if constexpr (S < 4) {
+    sa = mfma16(qa[S], score_b<M, S>(kc, cbh), sa);
+    score_steps<M, S + 1>(sa, qa, kc, cbh);
+  }
+}
 
-  // ---- set-up: fp16 codebook, rotated queries, per-group <q', o'_g>
-  const uint32_t* cbg = reinterpret_cast<const uint32_t*>(p.table + kTabCodebookH);
-  for (int i = tid; i < kCodes * CW; i += kThreads) cbh[i] = cbg[i];
-  for (int i = tid; i < kHB * kD; i += kThreads) {
-    const int h = i / kD, c = i % kD;
-    qr[h][c] = h < nh ? h2f(p.q[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c]) : 0.f;
-  }
-  __syncthreads();
-#pragma unroll 1
-  for (int st = 1; st < kD; st <<= 1) {
-    for (int i = tid; i < kHB * kD / 2; i += kThreads) {
-      const int h = i / (kD / 2), pr = i % (kD / 2);
-      const int k = ((pr / st) * 2 * st) + (pr % st);
-      const float a = qr[h][k], bb = qr[h][k + st];
-      qr[h][k] = a + bb;
-      qr[h][k + st] = a - bb;
-    }
-    __syncthreads();
-  }
-  for (int i = tid; i < kHB * kD; i += kThreads) qr[i / kD][i % kD] *= kInvSqrtD;
-  __syncthreads();
+__device__ __forceinline__ float dpp_row_shr4(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+}
 
-  const int ng = (c1 - c0) / G;
-  const uint16_t* ksrow = p.ks + row * (p.cap / G) * kD;
-  for (int pair = wave; pair < ng * kHB; pair += kWaves) {
-    const int g = pair / kHB, h = pair % kHB;
-    const uint16_t* o = ksrow + static_cast<int64_t>(c0 / G + g) * kD;
-    float s = qr[h][lane] * h2f(o[lane]) + qr[h][lane + 64] * h2f(o[lane + 64]);
-    s = wave_sum(s);
-    if (lane == 0) qo[g][h] = s;
-  }
-  // MFMA A operand, one per 16-channel step: rows 0..3 = fp16(q'_h),
-  // rows 8..11 = fp16(q'_h - fp16(q'_h)) (so the pair carries ~22 bits), other
-  // rows zero; lane (row t32, channels 16 s + 8 hf .. + 7)
-  u32x4 qa[8];
-  {
-    const bool is_hi = t32 < kHB, is_lo = t32 >= 8 && t32 < 8 + kHB;
-    const int hq = is_hi ? t32 : (is_lo ? t32 - 8 : 0);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      uint32_t wv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t pk = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float v = qr[hq][16 * st + 8 * hf + 2 * i + e];
-          const uint16_t hi = f2h(v);
-          const uint16_t lo = f2h(v - h2f(hi));
-          const uint16_t val = is_hi ? hi : (is_lo ? lo : 0);
-          pk |= static_cast<uint32_t>(val) << (16 * e);
-        }
-        wv[i] = pk;
-      }
-      qa[st] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-    }
-  }
-  __syncthreads();
-
-  // ---- per-wave online softmax over 64-token tiles
-  const int u = lane & 7;        // 16-channel unit (value phase)
-  const int slot = lane >> 3;    // token slot (value phase)
-  const int sh_h = slot >> 1;                 // shift term: this lane's head
-  const int sh_c = 16 * u + 8 * (slot & 1);   // and its 8 channels
-  float m_run[kHB], l_lane[kHB];
-  float acc[kHB][16];
-  float sh[8];
-#pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    m_run[h] = -__builtin_huge_valf();
-    l_lane[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sh[i] = 0.f;
-
-  const uint8_t* kcrow = p.kc + row * p.cap * CODE_BYTES;
-  const uint8_t* vcrow = p.vc + row * p.cap * CODE_BYTES;
-  const uint32_t* kmrow = reinterpret_cast<const uint32_t*>(p.km + row * p.cap * 2);
-  const uint32_t* vmrow = reinterpret_cast<const uint32_t*>(p.vm + row * p.cap * 2);
-  const uint16_t* vsrow = p.vs + row * (p.cap / G) * kD;
-
-  TileData cur;
-  if (c0 + 64 * wave < c1)
-    load_tile<M>(cur, c0 + 64 * wave, c1, lane, u, slot, sh_c, kcrow, vcrow, kmrow, vmrow,
-                 vsrow + static_cast<int64_t>((c0 + 64 * wave) / G) * kD);
-  for (int t0 = c0 + 64 * wave; t0 < c1; t0 += 64 * kWaves) {
-    TileData nxt;
-    const int tn = t0 + 64 * kWaves;
-    if (tn < c1)
-      load_tile<M>(nxt, tn, c1, lane, u, slot, sh_c, kcrow, vcrow, kmrow, vmrow,
-                   vsrow + static_cast<int64_t>(tn / G) * kD);
-    // -- scores on MFMA: block bk covers tokens t0 + 32 bk + t32
-    float sblk[2][kHB];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      uint32_t w8[8];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        w8[4 * i] = cur.kc[bk][i].x;
-        w8[4 * i + 1] = cur.kc[bk][i].y;
-        w8[4 * i + 2] = cur.kc[bk][i].z;
-        w8[4 * i + 3] = cur.kc[bk][i].w;
-      }
-      v16f sc = v16f{};
-      score_steps<M, 0>(sc, qa, w8, hf, cbh);
-#pragma unroll
-      for (int h = 0; h < kHB; ++h) sblk[bk][h] = sc[h] + sc[4 + h];   // hi + lo rows (lanes < 32)
-    }
-    // lanes 32..63 take block 1's tokens: lane l now holds token t0 + l
-    float dotq[kHB];
-#pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sblk[0][h]),
-                                                      __float_as_uint(sblk[1][h]), false, false);
-      dotq[h] = __uint_as_float(r[0]);
-    }
-    const int t = t0 + lane;
-    const bool valid = t < c1;
-    const uint32_t kmv = cur.km, vmv = cur.vm;
-    const int g = (t0 - c0) / G;  // one group per tile (64 divides G)
-    const float s1k = h2f(kmv & 0xffffu), s2k = h2f(kmv >> 16);
-    const float s1v = h2f(vmv & 0xffffu), s2v = h2f(vmv >> 16);
-    const float ks1 = p.scale * s1k;
-    float s[kHB];
-#pragma unroll
-    for (int h = 0; h < kHB; ++h) s[h] = ks1 * fmaf(s2k, dotq[h], qo[g][h]);
-    float pw[kHB], gs[kHB];
-#pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      if (!valid) s[h] = -__builtin_huge_valf();
-      const float mnew = fmaxf(m_run[h], wave_max_fast(s[h]));  // wave-uniform
-      if (mnew > m_run[h]) {
-        const float f = __expf(m_run[h] - mnew);
-        m_run[h] = mnew;
-        l_lane[h] *= f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[h][i] *= f;
-        if (sh_h == h) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sh[i] *= f;
-        }
-      }
-      pw[h] = valid ? __expf(s[h] - m_run[h]) : 0.f;
-      l_lane[h] += pw[h];
-      gs[h] = wave_sum_fast(pw[h] * s1v);
-    }
-    const float sv = s1v * s2v;
-    wbuf[wave][lane] = make_uint2(
-        static_cast<uint32_t>(f2h(pw[0] * sv)) | (static_cast<uint32_t>(f2h(pw[1] * sv)) << 16),
-        static_cast<uint32_t>(f2h(pw[2] * sv)) | (static_cast<uint32_t>(f2h(pw[3] * sv)) << 16));
-    // shift term p s1 o'_g: this lane owns head sh_h, channels sh_c .. sh_c + 7
-    {
-      const u32x4 o = cur.osh;
-      const float gsh = sh_h == 0 ? gs[0] : sh_h == 1 ? gs[1] : sh_h == 2 ? gs[2] : gs[3];
-      const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sh[2 * i] = fmaf(gsh, h2f(ow[i] & 0xffffu), sh[2 * i]);
-        sh[2 * i + 1] = fmaf(gsh, h2f(ow[i] >> 16), sh[2 * i + 1]);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // -- value phase: lane = (unit u, slot); token pairs (a, a + 8)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int ia = slot + 16 * k, ib = ia + 8;
-      const uint32_t va = cur.vc[2 * k], vb = cur.vc[2 * k + 1];
-      const uint2 wa = wbuf[wave][ia], wb = wbuf[wave][ib];
-      const uint32_t wp[kHB] = {pair_lo(wa.x, wb.x), pair_hi(wa.x, wb.x), pair_lo(wa.y, wb.y),
-                                pair_hi(wa.y, wb.y)};
-#pragma unroll
-      for (int pos = 0; pos < UPOS; ++pos) {
-        const uint32_t ca = (va >> (8 * pos)) & 0xffu, cb = (vb >> (8 * pos)) & 0xffu;
-        uint32_t xa[CW], xb[CW];
-#pragma unroll
-        for (int i = 0; i < CW; ++i) {
-          xa[i] = cbh[ca * CW + i];
-          xb[i] = cbh[cb * CW + i];
-        }
-#pragma unroll
-        for (int i = 0; i < CW; ++i) {
-          const uint32_t plo = pair_lo(xa[i], xb[i]), phi = pair_hi(xa[i], xb[i]);
-#pragma unroll
-          for (int h = 0; h < kHB; ++h) {
-            acc[h][pos * M + 2 * i] = dot2(wp[h], plo, acc[h][pos * M + 2 * i]);
-            acc[h][pos * M + 2 * i + 1] = dot2(wp[h], phi, acc[h][pos * M + 2 * i + 1]);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    cur = nxt;
-  }
-
-  // ---- merge: slots inside each wave, then the waves
-#pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    l_lane[h] = wave_sum(l_lane[h]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = acc[h][i];
-      v += __shfl_xor(v, 8, kWave);
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      acc[h][i] = v;
-    }
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int h = 0; h < kHB; ++h)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) wacc[wave][h][16 * u + i] = acc[h][i];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      wm[wave][h] = m_run[h];
-      wl[wave][h] = l_lane[h];
-    }
-  }
+__device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // the shift-term accumulators: each (head, channel) of a wave's row has
-  // exactly one owner lane, so a plain read-modify-write is race free
-#pragma unroll
-  for (int i = 0; i < 8; ++i) wacc[wave][sh_h][sh_c + i] += sh[i];
-  __syncthreads();
-  for (int idx = tid; idx < kHB * kD; idx += kThreads) {
-    const int h = idx / kD, c = idx % kD;
-    float M_ = -__builtin_huge_valf();
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, wm[w][h]);
-    float a = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float e = wm[w][h] == -__builtin_huge_valf() ? 0.f : __expf(wm[w][h] - M_);
-      a = fmaf(e, wacc[w][h][c], a);
-      l = fmaf(e, wl[w][h], l);
-    }
-    if (h < nh) {
-      float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * p.n_split + split) * kPartStride;
-      dst[c] = a;
-      if (c == 0) {
-        dst[128] = M_;
-        dst[129] = l;
-      }
-    }
-  }
 }
 
-struct CombineParams {
-  const uint16_t* q;
-  const uint16_t* kr;
-  const uint16_t* vr;
-  const float* work;
-  float* out;
-  int Hq, Hkv, grp, hblocks, n_resid, n_split;
-  int64_t rcap;
-  float scale;
-};
-
-constexpr int kCombThreads = 256;
-constexpr int kMaxResid = 1024;
-
-__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParams p) {
-  __shared__ float qf[kHB][kD];
-  __shared__ float sres[kHB][kMaxResid];
-  __shared__ float rot[kHB][kD];
-  __shared__ float red[kCombThreads / kWave][kHB];
+// The fp16 residual window of one (batch, kv head, head block): exact
+// scores and values in the original domain, written as partial n_split.
+__device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh, int hb) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  const int kvh = blockIdx.x / p.hblocks;
-  const int hb = blockIdx.x - kvh * p.hblocks;
-  const int b = blockIdx.y;
   const int h0 = kvh * p.grp + hb * kHB;
   const int nh = min(kHB, p.grp - hb * kHB);
   const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;
   const uint16_t* krow = p.kr + row * p.rcap * kD;
   const uint16_t* vrow = p.vr + row * p.rcap * kD;
+  const int nr = p.n_resid;
+  const float qscale = p.scale * kLog2e;   // scores in base-2 units
 
-  for (int i = tid; i < kHB * kD; i += kCombThreads) {
+  for (int i = tid; i < kHB * kD; i += kThreads) {
     const int h = i / kD, c = i % kD;
-    qf[h][c] = h < nh ? h2f(p.q[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c]) : 0.f;
+    sm.qf[h][c] = h < nh ? qscale * h2f(p.q[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c]) : 0.f;
   }
   __syncthreads();
-
-  // residual scores
-  for (int r = tid; r < p.n_resid; r += kCombThreads) {
+  for (int r = tid; r < nr; r += kThreads) {
     float s[kHB] = {0.f, 0.f, 0.f, 0.f};
     const uint4* kp = reinterpret_cast<const uint4*>(krow + static_cast<int64_t>(r) * kD);
 #pragma unroll 4
@@ -483,96 +245,449 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParam
         const float a = h2f(uu[k] & 0xffffu), bb = h2f(uu[k] >> 16);
         const int c = 8 * i + 2 * k;
 #pragma unroll
-        for (int h = 0; h < kHB; ++h) s[h] = fmaf(qf[h][c], a, fmaf(qf[h][c + 1], bb, s[h]));
+        for (int h = 0; h < kHB; ++h) s[h] = fmaf(sm.qf[h][c], a, fmaf(sm.qf[h][c + 1], bb, s[h]));
       }
     }
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) sres[h][r] = s[h] * p.scale;
+    for (int h = 0; h < kHB; ++h) sm.sres[h][r] = s[h];
   }
   __syncthreads();
   float mres[kHB], lres[kHB];
 #pragma unroll
   for (int h = 0; h < kHB; ++h) {
     float mx = -__builtin_huge_valf();
-    for (int r = tid; r < p.n_resid; r += kCombThreads) mx = fmaxf(mx, sres[h][r]);
+    for (int r = tid; r < nr; r += kThreads) mx = fmaxf(mx, sm.sres[h][r]);
     mx = wave_max(mx);
-    if (lane == 0) red[wave][h] = mx;
+    if (lane == 0) sm.red[wave][h] = mx;
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < kHB; ++h) {
-    float mx = red[0][h];
+    float mx = sm.red[0][h];
 #pragma unroll
-    for (int w = 1; w < kCombThreads / kWave; ++w) mx = fmaxf(mx, red[w][h]);
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.red[w][h]);
     mres[h] = mx;
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < kHB; ++h) {
     float ls = 0.f;
-    for (int r = tid; r < p.n_resid; r += kCombThreads) {
-      const float e = __expf(sres[h][r] - mres[h]);
-      sres[h][r] = e;
+    for (int r = tid; r < nr; r += kThreads) {
+      const float e = exp2_fast(sm.sres[h][r] - mres[h]);
+      sm.sres[h][r] = e;
       ls += e;
     }
     ls = wave_sum(ls);
-    if (lane == 0) red[wave][h] = ls;
+    if (lane == 0) sm.red[wave][h] = ls;
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < kHB; ++h) {
     float ls = 0.f;
 #pragma unroll
-    for (int w = 0; w < kCombThreads / kWave; ++w) ls += red[w][h];
+    for (int w = 0; w < kWaves; ++w) ls += sm.red[w][h];
     lres[h] = ls;
   }
-
-  // merge: every thread owns (h, c) for two (h, c) pairs
-  float res_acc[2], scale_res[2], L[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int idx = tid + k * kCombThreads;
+    const int idx = tid + k * kThreads;
     const int h = idx / kD, c = idx % kD;
-    float ra = 0.f;
-    for (int r = 0; r < p.n_resid; ++r) ra = fmaf(sres[h][r], h2f(vrow[static_cast<int64_t>(r) * kD + c]), ra);
-    float M = mres[h];
-    const float* part = p.work + (static_cast<int64_t>(b) * p.Hq + h0 + min(h, nh - 1)) * p.n_split * kPartStride;
-    for (int i = 0; i < p.n_split; ++i) M = fmaxf(M, part[i * kPartStride + 128]);
-    float a = 0.f, l = 0.f;
-    for (int i = 0; i < p.n_split; ++i) {
-      const float e = __expf(part[i * kPartStride + 128] - M);
-      a = fmaf(e, part[i * kPartStride + c], a);
-      l = fmaf(e, part[i * kPartStride + 129], l);
+    float a = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < nr; ++r) a = fmaf(sm.sres[h][r], h2f(vrow[static_cast<int64_t>(r) * kD + c]), a);
+    float mh = mres[0], lh = lres[0];
+#pragma unroll
+    for (int kk = 1; kk < kHB; ++kk) {
+      mh = h == kk ? mres[kk] : mh;
+      lh = h == kk ? lres[kk] : lh;
     }
-    const float er = __expf(mres[h] - M);
-    rot[h][c] = a;
-    res_acc[k] = ra;
-    scale_res[k] = er;
-    L[k] = fmaf(er, lres[h], l);
-  }
-  __syncthreads();
-#pragma unroll 1
-  for (int st = 1; st < kD; st <<= 1) {
-    const int h = tid / (kD / 2), pr = tid % (kD / 2);
-    const int i = ((pr / st) * 2 * st) + (pr % st);
-    const float a = rot[h][i], bb = rot[h][i + st];
-    rot[h][i] = a + bb;
-    rot[h][i + st] = a - bb;
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int idx = tid + k * kCombThreads;
-    const int h = idx / kD, c = idx % kD;
-    if (h < nh)
-      p.out[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c] =
-          fmaf(rot[h][c], kInvSqrtD, scale_res[k] * res_acc[k]) / L[k];
+    if (h < nh) {
+      float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * (p.n_split + 1) + p.n_split) * kPartStride;
+      dst[c] = a;
+      if (c == 0) {
+        dst[128] = mh;
+        dst[129] = lh;
+      }
+    }
   }
 }
 
 template <int M, int G>
+__global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(SplitParams p) {
+  constexpr int CB = kD / M;            // code bytes per token
+  constexpr int TPG = G / kTile;        // tiles per group
+  __shared__ AttnSmem smem;
+  SplitSmem& sm = smem.s;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int R = lane >> 4, c16 = lane & 15;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y / p.hblocks;
+  const int hb = blockIdx.y - kvh * p.hblocks;
+  const int b = blockIdx.z;
+  if (split == p.n_split) {
+    resid_block(p, smem.r, b, kvh, hb);
+    return;
+  }
+  const int h0 = kvh * p.grp + hb * kHB;
+  const int nh = min(kHB, p.grp - hb * kHB);
+  const int c0 = split * p.chunk;
+  const int c1 = min(p.n_quant, c0 + p.chunk);
+  const int ntiles = (c1 - c0) / kTile;   // chunks hold whole groups, groups whole tiles
+  const int ng = (c1 - c0) / G;
+  const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;  // (b, kv head) cache row
+  const uint16_t* ksg = p.ks + (row * (p.cap / G) + c0 / G) * kD;
+  const uint16_t* vsg = p.vs + (row * (p.cap / G) + c0 / G) * kD;
+
+  // ---- set-up: fp16 codebook, rotated queries (wave = head), zero weight slots
+  {
+    const uint32_t* cbg = reinterpret_cast<const uint32_t*>(p.table + kTabCodebookH);
+    for (int i = tid; i < kCodes * M / 2; i += kThreads) sm.cbh[i] = cbg[i];
+    float x0 = 0.f, x1 = 0.f;
+    if (wave < nh) {
+      const uint32_t qq =
+          reinterpret_cast<const uint32_t*>(p.q + (static_cast<int64_t>(b) * p.Hq + h0 + wave) * kD)[lane];
+      x0 = h2f(qq & 0xffffu);
+      x1 = h2f(qq >> 16);
+    }
+    // Walsh-Hadamard transform, channels 2 lane and 2 lane + 1 in this lane
+    const float u0 = x0 + x1, u1 = x0 - x1;
+    x0 = u0;
+    x1 = u1;
+#pragma unroll
+    for (int e = 1; e < kWave; e <<= 1) {
+      const float y0 = __shfl_xor(x0, e, kWave), y1 = __shfl_xor(x1, e, kWave);
+      const bool up = (lane & e) != 0;
+      x0 = up ? y0 - x0 : x0 + y0;
+      x1 = up ? y1 - x1 : x1 + y1;
+    }
+    sm.qr[wave][2 * lane] = x0 * kInvSqrtD;
+    sm.qr[wave][2 * lane + 1] = x1 * kInvSqrtD;
+    *reinterpret_cast<u32x4*>(&sm.wrow[wave][lane][8]) = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  // <q'_h, o'_g> for every group of the chunk, one thread per (g, h)
+  for (int idx = tid; idx < ng * kHB; idx += kThreads) {
+    const int g = idx / kHB, h = idx % kHB;
+    const uint4* o = reinterpret_cast<const uint4*>(ksg + static_cast<int64_t>(g) * kD);
+    float s = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < kD / 8; ++i) {
+      const uint4 w = o[i];
+      const uint32_t uu[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s = fmaf(sm.qr[h][8 * i + 2 * k], h2f(uu[k] & 0xffffu), s);
+        s = fmaf(sm.qr[h][8 * i + 2 * k + 1], h2f(uu[k] >> 16), s);
+      }
+    }
+    sm.qo[g][h] = s;
+  }
+  // score A operand per step s: row = slot c16 (0..3: fp16(q'_h), 4..7:
+  // fp16(q'_h - fp16(q'_h)), the pair carries ~22 bits; 8..15: 0), K index
+  // 8R + v = channel 32R + 8s + v
+  u32x4 qa[4];
+  {
+    const int hq = c16 & 3;
+    const bool is_hi = c16 < 4, is_lo = c16 >= 4 && c16 < 8;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float v = sm.qr[hq][32 * R + 8 * s + 2 * i + e];
+          const uint16_t hi = f2h(v);
+          const uint16_t lo = f2h(v - h2f(hi));
+          const uint16_t val = is_hi ? hi : (is_lo ? lo : 0);
+          pk |= static_cast<uint32_t>(val) << (16 * e);
+        }
+        wv[i] = pk;
+      }
+      qa[s] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    }
+  }
+  __syncthreads();
+
+  // ---- per-wave online softmax over the wave's tiles
+  float m_run[kHB], l_lane[kHB];
+#pragma unroll
+  for (int h = 0; h < kHB; ++h) {
+    m_run[h] = -__builtin_huge_valf();
+    l_lane[h] = 0.f;
+  }
+  v4f acc[8];   // rows: channels 32R + 4cb + j; columns: weight slot c16
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int slot_head = c16 & 3;
+  const float qscale = p.scale * kLog2e;
+  const int a4 = lane & 3, k4 = (lane & 15) >> 2;
+
+  const uint8_t* kcrow = p.kc + row * p.cap * CB + static_cast<int64_t>(c0) * CB;
+  const uint8_t* vcrow = p.vc + row * p.cap * CB + static_cast<int64_t>(c0) * CB;
+  const uint32_t* kmrow = reinterpret_cast<const uint32_t*>(p.km + row * p.cap * 2) + c0;
+  const uint32_t* vmrow = reinterpret_cast<const uint32_t*>(p.vm + row * p.cap * 2) + c0;
+  const uint32_t koff = c16 * CB + (M == 4 ? 8 : 4) * R;
+  const uint32_t voff = (8 * R + k4) * CB + (M == 4 ? 8 : 4) * a4;
+  const uint32_t cbh_base = lds_addr(sm.cbh);
+  const uint32_t wtr = lds_addr(&sm.wrow[wave][8 * R + k4][4 * a4]);
+
+  auto load = [&](TileData<M>& d, int tau) {
+    const int t0 = tau * kTile;
+    load_tile<M>(d, kcrow + t0 * CB, vcrow + t0 * CB, kmrow + t0, vmrow + t0, koff, voff, lane);
+  };
+
+  auto process = [&](const TileData<M>& d, int tau) {
+    // -- scores
+    v4f sacc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      sacc[tb] = v4f{0.f, 0.f, 0.f, 0.f};
+      score_steps<M, 0>(sacc[tb], qa, d.kc[tb], sm.cbh);
+    }
+    // rows 0..3 (lanes 0..15) hold high-part scores of heads 0..3, rows 4..7
+    // (lanes 16..31) low-part ones; swap so that lane l holds token l
+    float dot[kHB];
+#pragma unroll
+    for (int j = 0; j < kHB; ++j) {
+      const auto r01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sacc[0][j]),
+                                                        __float_as_uint(sacc[1][j]), false, false);
+      const auto r23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sacc[2][j]),
+                                                        __float_as_uint(sacc[3][j]), false, false);
+      const float t01 = __uint_as_float(r01[0]) + __uint_as_float(r01[1]);
+      const float t23 = __uint_as_float(r23[0]) + __uint_as_float(r23[1]);
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t01), __float_as_uint(t23), false, false);
+      dot[j] = __uint_as_float(r[0]);
+    }
+    const int g = tau / TPG;
+    const float4 qo4 = *reinterpret_cast<const float4*>(&sm.qo[g][0]);
+    const float qov[kHB] = {qo4.x, qo4.y, qo4.z, qo4.w};
+    const float s1k = h2f(d.km & 0xffffu), s2k = h2f(d.km >> 16);
+    const float s1v = h2f(d.vm & 0xffffu), s2v = h2f(d.vm >> 16);
+    const float ks = qscale * s1k;
+    float s[kHB];
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) s[h] = ks * fmaf(s2k, dot[h], qov[h]);
+    // -- running max, raised only when a score exceeds it
+    bool raised = false;
+    float fl = 1.f;
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      if (__ballot(s[h] > m_run[h])) {
+        const float mn = fmaxf(m_run[h], wave_max_fast(s[h]));
+        const float f = exp2_fast(m_run[h] - mn);
+        m_run[h] = mn;
+        l_lane[h] *= f;
+        fl = slot_head == h ? f : fl;
+        raised = true;
+      }
+    }
+    if (raised) {
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) acc[cb] *= fl;
+    }
+    // -- weights: p s1 s2' as fp16 high + low parts into the wave's rows;
+    //    p s1 per head summed over the tile for the shift term
+    float sp[kHB];
+    uint32_t wk[4];
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      const float pw = exp2_fast(s[h] - m_run[h]);
+      l_lane[h] += pw;
+      sp[h] = pw * s1v;
+      const float w = sp[h] * s2v;
+      const _Float16 hi = static_cast<_Float16>(w);
+      const _Float16 lo = static_cast<_Float16>(w - static_cast<float>(hi));
+      const uint32_t hb16 = __builtin_bit_cast(uint16_t, hi), lb16 = __builtin_bit_cast(uint16_t, lo);
+      if (h & 1) {
+        wk[h >> 1] |= hb16 << 16;
+        wk[2 + (h >> 1)] |= lb16 << 16;
+      } else {
+        wk[h >> 1] = hb16;
+        wk[2 + (h >> 1)] = lb16;
+      }
+    }
+    *reinterpret_cast<u32x4*>(&sm.wrow[wave][lane][0]) = u32x4{wk[0], wk[1], wk[2], wk[3]};
+    {
+      // four wave sums at once: halves, then rows, then within rows; row R
+      // ends with head (0, 2, 1, 3)[R]
+      const auto x01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sp[0]), __float_as_uint(sp[1]), false, false);
+      const auto x23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sp[2]), __float_as_uint(sp[3]), false, false);
+      const float u = __uint_as_float(x01[0]) + __uint_as_float(x01[1]);
+      const float w = __uint_as_float(x23[0]) + __uint_as_float(x23[1]);
+      const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(w), false, false);
+      float z = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      auto dpp = [](float v, auto ctrl_c) {
+        constexpr int ctrl = decltype(ctrl_c)::value;
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false));
+      };
+      z += dpp(z, std::integral_constant<int, 0xB1>{});
+      z += dpp(z, std::integral_constant<int, 0x4E>{});
+      z += dpp(z, std::integral_constant<int, 0x124>{});
+      z += dpp(z, std::integral_constant<int, 0x128>{});
+      if (c16 == 0) sm.ssum[tau][((R & 1) << 1) | (R >> 1)] = z;
+      if (lane == 0) *reinterpret_cast<float4*>(&sm.smax[tau][0]) = make_float4(m_run[0], m_run[1], m_run[2], m_run[3]);
+    }
+    wave_lds_sync();
+    // -- values: acc[cb] += C^T (32 channels x 32 tokens) W (32 tokens x 16 slots)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint2 w0 = ds_tr16(wtr + (32 * kb) * 32);
+      const uint2 w1 = ds_tr16(wtr + (32 * kb + 4) * 32);
+      const u32x4 bw = u32x4{w0.x, w0.y, w1.x, w1.y};
+      value_steps<M, 0>(acc, d, kb, bw, cbh_base);
+    }
+    wave_lds_sync();
+  };
+
+  {
+    TileData<M> ta, tb;
+    int tau = wave;
+    if (tau < ntiles) load(ta, tau);
+    while (tau < ntiles) {
+      if (tau + kWaves < ntiles) load(tb, tau + kWaves);
+      process(ta, tau);
+      tau += kWaves;
+      if (tau >= ntiles) break;
+      if (tau + kWaves < ntiles) load(ta, tau + kWaves);
+      process(tb, tau);
+      tau += kWaves;
+    }
+  }
+
+  // ---- merge: high + low slots (lanes c16 = 4..7 end with the sum), waves
+  float* wacc = reinterpret_cast<float*>(&sm.wrow[wave][0][0]);   // [kHB][kD]
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[cb][j] += dpp_row_shr4(acc[cb][j]);
+  wave_lds_sync();
+  if (c16 >= 4 && c16 < 8) {
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      *reinterpret_cast<v4f*>(&wacc[(c16 - 4) * kD + 32 * R + 4 * cb]) = acc[cb];
+  }
+  float lsum[kHB];
+#pragma unroll
+  for (int h = 0; h < kHB; ++h) lsum[h] = wave_sum_fast(l_lane[h]);
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      sm.wm[wave][h] = m_run[h];
+      sm.wl[wave][h] = lsum[h];
+    }
+  }
+  __syncthreads();
+  float Mh[kHB];
+#pragma unroll
+  for (int h = 0; h < kHB; ++h) {
+    float mx = sm.wm[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.wm[w][h]);
+    Mh[h] = mx;
+  }
+  for (int idx = tid; idx < ng * kHB; idx += kThreads) {
+    const int g = idx / kHB, h = idx % kHB;
+    float mh = Mh[0];
+#pragma unroll
+    for (int k = 1; k < kHB; ++k) mh = h == k ? Mh[k] : mh;
+    float S = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPG; ++t) {
+      S = fmaf(sm.ssum[g * TPG + t][h], exp2_fast(sm.smax[g * TPG + t][h] - mh), S);
+    }
+    sm.sg[g][h] = S;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + k * kThreads;
+    const int h = idx / kD, c = idx % kD;   // h is uniform in a wave
+    float mh = Mh[0];
+#pragma unroll
+    for (int kk = 1; kk < kHB; ++kk) mh = h == kk ? Mh[kk] : mh;
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.wm[w][h];
+      const float e = mw == -__builtin_huge_valf() ? 0.f : exp2_fast(mw - mh);
+      a = fmaf(e, reinterpret_cast<const float*>(&sm.wrow[w][0][0])[h * kD + c], a);
+      l = fmaf(e, sm.wl[w][h], l);
+    }
+#pragma unroll 8
+    for (int g = 0; g < ng; ++g) a = fmaf(sm.sg[g][h], h2f(vsg[static_cast<int64_t>(g) * kD + c]), a);
+    if (h < nh) {
+      float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * (p.n_split + 1) + split) * kPartStride;
+      dst[c] = a;
+      if (c == 0) {
+        dst[128] = mh;
+        dst[129] = l;
+      }
+    }
+  }
+}
+
+struct CombineParams {
+  const float* work;
+  float* out;
+  int Hq, n_split;
+};
+
+constexpr int kCombThreads = 256;
+
+// One wave per (batch, query head): lane holds rotated channels 2 lane and
+// 2 lane + 1.
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParams p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int hq = blockIdx.x * (kCombThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (hq >= p.Hq) return;
+  const int64_t gh = static_cast<int64_t>(blockIdx.y) * p.Hq + hq;
+  const float* part = p.work + gh * (p.n_split + 1) * kPartStride;
+  const float ninf = -__builtin_huge_valf();
+  float M = ninf;
+  for (int i = 0; i <= p.n_split; ++i) M = fmaxf(M, part[i * kPartStride + 128]);
+  float a0 = 0.f, a1 = 0.f, L = 0.f;
+  for (int i = 0; i < p.n_split; ++i) {
+    const float* pi = part + i * kPartStride;
+    const float mi = pi[128];
+    const float e = mi == ninf ? 0.f : exp2_fast(mi - M);
+    L = fmaf(e, pi[129], L);
+    const float2 v = reinterpret_cast<const float2*>(pi)[lane];
+    a0 = fmaf(e, v.x, a0);
+    a1 = fmaf(e, v.y, a1);
+  }
+  // inverse rotation (the transform is its own inverse up to 1/sqrt(d))
+  {
+    const float u0 = a0 + a1, u1 = a0 - a1;
+    a0 = u0;
+    a1 = u1;
+#pragma unroll
+    for (int e = 1; e < kWave; e <<= 1) {
+      const float y0 = __shfl_xor(a0, e, kWave), y1 = __shfl_xor(a1, e, kWave);
+      const bool up = (lane & e) != 0;
+      a0 = up ? y0 - a0 : a0 + y0;
+      a1 = up ? y1 - a1 : a1 + y1;
+    }
+  }
+  const float* pr = part + p.n_split * kPartStride;
+  const float mr = pr[128];
+  const float er = mr == ninf ? 0.f : exp2_fast(mr - M);
+  L = fmaf(er, pr[129], L);
+  const float2 rv = reinterpret_cast<const float2*>(pr)[lane];
+  const float inv = 1.f / L;
+  float2 o;
+  o.x = fmaf(a0, kInvSqrtD, er * rv.x) * inv;
+  o.y = fmaf(a1, kInvSqrtD, er * rv.y) * inv;
+  reinterpret_cast<float2*>(p.out + gh * kD)[lane] = o;
+}
+
+template <int M, int G>
 hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s) {
-  dim3 grid(a.n_split, a.Hkv * sp.hblocks, a.B);
+  dim3 grid(a.n_split + 1, a.Hkv * sp.hblocks, a.B);
   hipLaunchKernelGGL((attn_split_kernel<M, G>), grid, dim3(kThreads), 0, s, sp);
   return hipGetLastError();
 }
@@ -587,8 +702,11 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int* n_split
   }
   const int grp = Hq / Hkv;
   const int64_t units = static_cast<int64_t>(B) * Hkv * ((grp + kHB - 1) / kHB);
-  const int max_split = (n_quant + kMinChunk - 1) / kMinChunk;
-  int64_t want = (3072 + units - 1) / units;  // about four rounds of three workgroups per CU
+  // one round of resident workgroups, one slot per unit kept for its
+  // residual-window workgroup
+  const int64_t slots = static_cast<int64_t>(kPlanCUs) * kBlocksPerCU;
+  int64_t want = slots / units - 1;
+  const int64_t max_split = (n_quant + kMinChunk - 1) / kMinChunk;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   int64_t c = (n_quant + want - 1) / want;
@@ -599,25 +717,26 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int* n_split
 }
 
 size_t attn_workspace_bytes(int B, int Hq, int n_split) {
-  return static_cast<size_t>(B) * Hq * (n_split > 0 ? n_split : 1) * kPartStride * sizeof(float);
+  return static_cast<size_t>(B) * Hq * (n_split + 1) * kPartStride * sizeof(float);
 }
 
 hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s) {
   const int grp = a.Hq / a.Hkv;
   const int hblocks = (grp + kHB - 1) / kHB;
-  if (a.n_split > 0) {
-    SplitParams sp{a.q, a.kc, a.vc, a.km, a.vm, a.ks, a.vs, static_cast<const uint8_t*>(a.table),
-                   a.work, a.Hq, a.Hkv, grp, hblocks, a.n_quant, a.n_split, a.chunk, a.cap, a.scale};
-    hipError_t e;
-    if (a.sub_dim == 4)
-      e = a.group_size == 128 ? split_launch<4, 128>(a, sp, s) : split_launch<4, 256>(a, sp, s);
-    else
-      e = a.group_size == 128 ? split_launch<8, 128>(a, sp, s) : split_launch<8, 256>(a, sp, s);
-    if (e != hipSuccess) return e;
-  }
-  CombineParams cp{a.q, a.kr, a.vr, a.work, a.out, a.Hq, a.Hkv, grp, hblocks, a.n_resid,
-                   a.n_split, a.rcap, a.scale};
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.Hkv * hblocks, a.B), dim3(kCombThreads), 0, s, cp);
+  SplitParams sp{a.q,     a.kc,       a.vc,    a.km,      a.vm,      a.ks,    a.vs,
+                 a.kr,    a.vr,       static_cast<const uint8_t*>(a.table), a.work,
+                 a.Hq,    a.Hkv,      grp,     hblocks,   a.n_quant, a.n_split, a.chunk,
+                 a.n_resid, a.cap,    a.rcap,  a.scale};
+  hipError_t e;
+  if (a.sub_dim == 4)
+    e = a.group_size == 128 ? split_launch<4, 128>(a, sp, s) : split_launch<4, 256>(a, sp, s);
+  else
+    e = a.group_size == 128 ? split_launch<8, 128>(a, sp, s) : split_launch<8, 256>(a, sp, s);
+  if (e != hipSuccess) return e;
+  CombineParams cp{a.work, a.out, a.Hq, a.n_split};
+  const int per_block = kCombThreads / kWave;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((a.Hq + per_block - 1) / per_block, a.B),
+                     dim3(kCombThreads), 0, s, cp);
   return hipGetLastError();
 }
 
