@@ -27,8 +27,8 @@
 //              p s1 s2' from a per-wave LDS row buffer.
 //     shift    the tile's sum of p s1 per head (fp32) is kept in LDS with the
 //              max it refers to and applied to the group shifts at the end.
-//   Workgroup index n_split along x handles the fp16 residual window instead
-//   (exact scores, original domain).
+//   The workgroup of chunk 0 first takes the fp16 residual window (exact
+//   scores, original domain), written as partial n_split.
 // attn_combine_kernel: one wave per (batch, query head): log-sum-exp merge of
 //   the chunk partials, inverse rotation, residual partial, normalization.
 #include <type_traits>
@@ -50,7 +50,8 @@ constexpr int kMaxGroups = kMaxChunk / 128;
 constexpr int kMinChunk = 512;
 constexpr int kMaxResid = 1024;
 constexpr int kPartStride = 132;     // acc[128], m, l, pad
-constexpr int kBlocksPerCU = 3;      // resident split workgroups per CU (VGPR bound)
+constexpr int kBlocksPerCU = 4;      // split workgroups one CU can hold (<= 128 VGPRs)
+constexpr int kPlanBlocksPerCU = 3;  // workgroups per CU the split count aims at (measured best)
 constexpr int kPlanCUs = 256;
 constexpr float kInvSqrtD = 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -78,8 +79,9 @@ struct SplitParams {
   float scale;
 };
 
+template <int M>
 struct SplitSmem {
-  uint32_t cbh[kCodes * 4];          // fp16 codebook: 8 (m = 4) or 16 (m = 8) bytes per code
+  uint32_t cbh[kCodes * M / 2];      // fp16 codebook, 2m bytes per code
   float qr[kHB][kD];                 // rotated queries
   float qo[kMaxGroups][kHB];         // <q'_h, o'_g> per group of the chunk
   float sg[kMaxGroups][kHB];         // per group: sum of p s1, relative to the final max
@@ -93,12 +95,13 @@ struct SplitSmem {
   float wl[kWaves][kHB];
 };
 struct ResidSmem {
-  float qf[kHB][kD];
-  float sres[kHB][kMaxResid];
+  float4 sres[kMaxResid];          // per token: scores, then weights, of the 4 heads
   float red[kWaves][kHB];
+  float vpart[kWaves][kHB][kD];
 };
+template <int M>
 union AttnSmem {
-  SplitSmem s;
+  SplitSmem<M> s;
   ResidSmem r;
 };
 
@@ -141,19 +144,26 @@ struct TileData {
   uint32_t km, vm;  // (s1, s2') of token `lane`
 };
 
+// The three parts of a tile are loaded separately, each right after the
+// last use of the current tile's part (a full phase ahead of the next use
+// with one set of registers).
 template <int M>
-__device__ __forceinline__ void load_tile(TileData<M>& d, const uint8_t* kb, const uint8_t* vb,
-                                          const uint32_t* kmb, const uint32_t* vmb, uint32_t koff,
-                                          uint32_t voff, int lane) {
-  constexpr int CB = kD / M;
+__device__ __forceinline__ void load_keys(TileData<M>& d, const uint8_t* kb, uint32_t koff) {
   using CT = typename TileData<M>::CT;
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
-    d.kc[tb] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(kb + koff + 16 * tb * CB));
+    d.kc[tb] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(kb + koff + 16 * tb * (kD / M)));
+}
+template <int M>
+__device__ __forceinline__ void load_values(TileData<M>& d, const uint8_t* vb, uint32_t voff) {
+  using CT = typename TileData<M>::CT;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     d.vc[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const CT*>(vb + voff + (32 * (i >> 1) + 4 * (i & 1)) * CB));
+        reinterpret_cast<const CT*>(vb + voff + (32 * (i >> 1) + 4 * (i & 1)) * (kD / M)));
+}
+template <int M>
+__device__ __forceinline__ void load_meta(TileData<M>& d, const uint32_t* kmb, const uint32_t* vmb, int lane) {
   d.km = __builtin_nontemporal_load(kmb + lane);
   d.vm = __builtin_nontemporal_load(vmb + lane);
 }
@@ -204,7 +214,6 @@ __device__ __forceinline__ void score_steps(v4f& sa, const u32x4 (&qa)[4], const
     score_steps<M, S + 1>(sa, qa, kc, cbh);
   }
 }
-
 __device__ __forceinline__ float dpp_row_shr4(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
 }
@@ -215,11 +224,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The fp16 residual window of one (batch, kv head, head block): exact
-// scores and values in the original domain, written as partial n_split.
+// The fp16 residual window of one (batch, kv head, head block), in the
+// original domain, written as partial n_split.  Scores: fp16 q and k are
+// exact MFMA inputs (fp32 sums); values: one thread per (channel pair,
+// token quarter), the quarters summed through LDS.
 __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh, int hb) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int R = lane >> 4, c16 = lane & 15;
   const int h0 = kvh * p.grp + hb * kHB;
   const int nh = min(kHB, p.grp - hb * kHB);
   const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;
@@ -227,86 +240,119 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
   const uint16_t* vrow = p.vr + row * p.rcap * kD;
   const int nr = p.n_resid;
   const float qscale = p.scale * kLog2e;   // scores in base-2 units
+  const float ninf = -__builtin_huge_valf();
 
-  for (int i = tid; i < kHB * kD; i += kThreads) {
-    const int h = i / kD, c = i % kD;
-    sm.qf[h][c] = h < nh ? qscale * h2f(p.q[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c]) : 0.f;
-  }
-  __syncthreads();
-  for (int r = tid; r < nr; r += kThreads) {
-    float s[kHB] = {0.f, 0.f, 0.f, 0.f};
-    const uint4* kp = reinterpret_cast<const uint4*>(krow + static_cast<int64_t>(r) * kD);
-#pragma unroll 4
-    for (int i = 0; i < kD / 8; ++i) {
-      const uint4 w = kp[i];
-      const uint32_t uu[4] = {w.x, w.y, w.z, w.w};
+  // A operand per step s: row c16 = head c16 (< nh), K index 8R + v =
+  // channel 32 s + 8R + v
+  u32x4 qa[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float a = h2f(uu[k] & 0xffffu), bb = h2f(uu[k] >> 16);
-        const int c = 8 * i + 2 * k;
+  for (int s = 0; s < 4; ++s)
+    qa[s] = c16 < nh ? *reinterpret_cast<const u32x4*>(
+                           p.q + (static_cast<int64_t>(b) * p.Hq + h0 + c16) * kD + 32 * s + 8 * R)
+                     : u32x4{0u, 0u, 0u, 0u};
+  // two 16-token blocks per wave and pass, all loads issued first
+  for (int tb = 2 * wave; tb * 16 < nr; tb += 2 * kWaves) {
+    u32x4 kb[2][4];
 #pragma unroll
-        for (int h = 0; h < kHB; ++h) s[h] = fmaf(sm.qf[h][c], a, fmaf(sm.qf[h][c + 1], bb, s[h]));
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int t = (tb + u) * 16 + c16;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kb[u][s] = t < nr ? *reinterpret_cast<const u32x4*>(krow + static_cast<int64_t>(t) * kD + 32 * s + 8 * R)
+                          : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) sm.sres[h][r] = s[h];
-  }
-  __syncthreads();
-  float mres[kHB], lres[kHB];
+    for (int u = 0; u < 2; ++u) {
+      const int t = (tb + u) * 16 + c16;
+      v4f d = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    float mx = -__builtin_huge_valf();
-    for (int r = tid; r < nr; r += kThreads) mx = fmaxf(mx, sm.sres[h][r]);
-    mx = wave_max(mx);
-    if (lane == 0) sm.red[wave][h] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    float mx = sm.red[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.red[w][h]);
-    mres[h] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    float ls = 0.f;
-    for (int r = tid; r < nr; r += kThreads) {
-      const float e = exp2_fast(sm.sres[h][r] - mres[h]);
-      sm.sres[h][r] = e;
-      ls += e;
+      for (int s = 0; s < 4; ++s) d = mfma16(qa[s], kb[u][s], d);
+      if (R == 0 && t < nr)
+        sm.sres[t] = make_float4(d[0] * qscale, d[1] * qscale, d[2] * qscale, d[3] * qscale);
     }
-    ls = wave_sum(ls);
-    if (lane == 0) sm.red[wave][h] = ls;
   }
   __syncthreads();
+  float mx[kHB] = {ninf, ninf, ninf, ninf};
+  for (int t = tid; t < nr; t += kThreads) {
+    const float4 v = sm.sres[t];
+    mx[0] = fmaxf(mx[0], v.x);
+    mx[1] = fmaxf(mx[1], v.y);
+    mx[2] = fmaxf(mx[2], v.z);
+    mx[3] = fmaxf(mx[3], v.w);
+  }
 #pragma unroll
   for (int h = 0; h < kHB; ++h) {
-    float ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) ls += sm.red[w][h];
-    lres[h] = ls;
+    mx[h] = wave_max_fast(mx[h]);
+    if (lane == 0) sm.red[wave][h] = mx[h];
   }
+  __syncthreads();
+  float mres[kHB];
+#pragma unroll
+  for (int h = 0; h < kHB; ++h) {
+    float m = sm.red[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, sm.red[w][h]);
+    mres[h] = m;
+  }
+  __syncthreads();
+  float ls[kHB] = {0.f, 0.f, 0.f, 0.f};
+  for (int t = tid; t < nr; t += kThreads) {
+    float4 v = sm.sres[t];
+    v.x = exp2_fast(v.x - mres[0]);
+    v.y = exp2_fast(v.y - mres[1]);
+    v.z = exp2_fast(v.z - mres[2]);
+    v.w = exp2_fast(v.w - mres[3]);
+    sm.sres[t] = v;
+    ls[0] += v.x;
+    ls[1] += v.y;
+    ls[2] += v.z;
+    ls[3] += v.w;
+  }
+#pragma unroll
+  for (int h = 0; h < kHB; ++h) {
+    ls[h] = wave_sum_fast(ls[h]);
+    if (lane == 0) sm.red[wave][h] = ls[h];
+  }
+  __syncthreads();
+  // values: this thread's channels 2 lane, 2 lane + 1 over tokens wave, wave + 4, ...
+  float a[kHB][2] = {};
+#pragma unroll 16
+  for (int t = wave; t < nr; t += kWaves) {
+    const uint32_t v = reinterpret_cast<const uint32_t*>(vrow + static_cast<int64_t>(t) * kD)[lane];
+    const float v0 = h2f(v & 0xffffu), v1 = h2f(v >> 16);
+    const float4 pv = sm.sres[t];
+    a[0][0] = fmaf(pv.x, v0, a[0][0]);
+    a[0][1] = fmaf(pv.x, v1, a[0][1]);
+    a[1][0] = fmaf(pv.y, v0, a[1][0]);
+    a[1][1] = fmaf(pv.y, v1, a[1][1]);
+    a[2][0] = fmaf(pv.z, v0, a[2][0]);
+    a[2][1] = fmaf(pv.z, v1, a[2][1]);
+    a[3][0] = fmaf(pv.w, v0, a[3][0]);
+    a[3][1] = fmaf(pv.w, v1, a[3][1]);
+  }
+#pragma unroll
+  for (int h = 0; h < kHB; ++h)
+    *reinterpret_cast<float2*>(&sm.vpart[wave][h][2 * lane]) = make_float2(a[h][0], a[h][1]);
+  __syncthreads();
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int idx = tid + k * kThreads;
-    const int h = idx / kD, c = idx % kD;
-    float a = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < nr; ++r) a = fmaf(sm.sres[h][r], h2f(vrow[static_cast<int64_t>(r) * kD + c]), a);
-    float mh = mres[0], lh = lres[0];
+    const int h = idx / kD, c = idx % kD;   // h is uniform in a wave
+    float acc = 0.f;
 #pragma unroll
-    for (int kk = 1; kk < kHB; ++kk) {
-      mh = h == kk ? mres[kk] : mh;
-      lh = h == kk ? lres[kk] : lh;
-    }
+    for (int w = 0; w < kWaves; ++w) acc += sm.vpart[w][h][c];
+    float mh = mres[0];
+#pragma unroll
+    for (int kk = 1; kk < kHB; ++kk) mh = h == kk ? mres[kk] : mh;
     if (h < nh) {
       float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * (p.n_split + 1) + p.n_split) * kPartStride;
-      dst[c] = a;
+      dst[c] = acc;
       if (c == 0) {
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) l += sm.red[w][h];
         dst[128] = mh;
-        dst[129] = lh;
+        dst[129] = l;
       }
     }
   }
@@ -316,8 +362,8 @@ template <int M, int G>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(SplitParams p) {
   constexpr int CB = kD / M;            // code bytes per token
   constexpr int TPG = G / kTile;        // tiles per group
-  __shared__ AttnSmem smem;
-  SplitSmem& sm = smem.s;
+  __shared__ AttnSmem<M> smem;
+  SplitSmem<M>& sm = smem.s;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -327,9 +373,12 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
   const int kvh = blockIdx.y / p.hblocks;
   const int hb = blockIdx.y - kvh * p.hblocks;
   const int b = blockIdx.z;
-  if (split == p.n_split) {
+  if (split == 0) {
+    // the residual window first: its load latency overlaps the other
+    // workgroups' work instead of ending the kernel
     resid_block(p, smem.r, b, kvh, hb);
-    return;
+    if (p.n_split == 0) return;
+    __syncthreads();   // the LDS is reused
   }
   const int h0 = kvh * p.grp + hb * kHB;
   const int nh = min(kHB, p.grp - hb * kHB);
@@ -433,15 +482,18 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
   const uint32_t* vmrow = reinterpret_cast<const uint32_t*>(p.vm + row * p.cap * 2) + c0;
   const uint32_t koff = c16 * CB + (M == 4 ? 8 : 4) * R;
   const uint32_t voff = (8 * R + k4) * CB + (M == 4 ? 8 : 4) * a4;
-  const uint32_t cbh_base = lds_addr(sm.cbh);
+  const uint32_t cbh_base = lds_addr(sm.cbh);   // codebook copy of this lane
   const uint32_t wtr = lds_addr(&sm.wrow[wave][8 * R + k4][4 * a4]);
 
-  auto load = [&](TileData<M>& d, int tau) {
-    const int t0 = tau * kTile;
-    load_tile<M>(d, kcrow + t0 * CB, vcrow + t0 * CB, kmrow + t0, vmrow + t0, koff, voff, lane);
-  };
-
-  auto process = [&](const TileData<M>& d, int tau) {
+  TileData<M> d;
+  for (int tau = wave; tau < ntiles; tau += kWaves) {
+    const int tn = tau + kWaves;
+    const bool more = tn < ntiles;
+    if (tau == wave) {
+      load_keys<M>(d, kcrow + tau * kTile * CB, koff);
+      load_meta<M>(d, kmrow + tau * kTile, vmrow + tau * kTile, lane);
+      load_values<M>(d, vcrow + tau * kTile * CB, voff);
+    }
     // -- scores
     v4f sacc[4];
 #pragma unroll
@@ -449,6 +501,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
       sacc[tb] = v4f{0.f, 0.f, 0.f, 0.f};
       score_steps<M, 0>(sacc[tb], qa, d.kc[tb], sm.cbh);
     }
+    if (more) load_keys<M>(d, kcrow + tn * kTile * CB, koff);
     // rows 0..3 (lanes 0..15) hold high-part scores of heads 0..3, rows 4..7
     // (lanes 16..31) low-part ones; swap so that lane l holds token l
     float dot[kHB];
@@ -468,6 +521,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
     const float qov[kHB] = {qo4.x, qo4.y, qo4.z, qo4.w};
     const float s1k = h2f(d.km & 0xffffu), s2k = h2f(d.km >> 16);
     const float s1v = h2f(d.vm & 0xffffu), s2v = h2f(d.vm >> 16);
+    if (more) load_meta<M>(d, kmrow + tn * kTile, vmrow + tn * kTile, lane);
     const float ks = qscale * s1k;
     float s[kHB];
 #pragma unroll
@@ -541,22 +595,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
       const u32x4 bw = u32x4{w0.x, w0.y, w1.x, w1.y};
       value_steps<M, 0>(acc, d, kb, bw, cbh_base);
     }
+    if (more) load_values<M>(d, vcrow + tn * kTile * CB, voff);
     wave_lds_sync();
-  };
-
-  {
-    TileData<M> ta, tb;
-    int tau = wave;
-    if (tau < ntiles) load(ta, tau);
-    while (tau < ntiles) {
-      if (tau + kWaves < ntiles) load(tb, tau + kWaves);
-      process(ta, tau);
-      tau += kWaves;
-      if (tau >= ntiles) break;
-      if (tau + kWaves < ntiles) load(ta, tau + kWaves);
-      process(tb, tau);
-      tau += kWaves;
-    }
   }
 
   // ---- merge: high + low slots (lanes c16 = 4..7 end with the sum), waves
@@ -687,7 +727,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParam
 
 template <int M, int G>
 hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s) {
-  dim3 grid(a.n_split + 1, a.Hkv * sp.hblocks, a.B);
+  dim3 grid(a.n_split > 0 ? a.n_split : 1, a.Hkv * sp.hblocks, a.B);
   hipLaunchKernelGGL((attn_split_kernel<M, G>), grid, dim3(kThreads), 0, s, sp);
   return hipGetLastError();
 }
@@ -702,10 +742,10 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int* n_split
   }
   const int grp = Hq / Hkv;
   const int64_t units = static_cast<int64_t>(B) * Hkv * ((grp + kHB - 1) / kHB);
-  // one round of resident workgroups, one slot per unit kept for its
-  // residual-window workgroup
-  const int64_t slots = static_cast<int64_t>(kPlanCUs) * kBlocksPerCU;
-  int64_t want = slots / units - 1;
+  // about three workgroups per CU in one round: every CU equally busy, with
+  // room left for one more workgroup per CU while the others finish
+  const int64_t slots = static_cast<int64_t>(kPlanCUs) * kPlanBlocksPerCU;
+  int64_t want = slots / units;
   const int64_t max_split = (n_quant + kMinChunk - 1) / kMinChunk;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;

@@ -84,6 +84,9 @@ def check(cache, q, heads=None, scale=None):
     (2, 4, 2, 1536, 33, 4, 256),       # G = 256, GQA 2:1
     (1, 8, 2, 2048, 64, 8, 128),       # 1-bit codes
     (1, 4, 1, 10240, 7, 4, 128),       # several chunks, ragged chunk end
+    (1, 4, 1, 128, 200, 4, 128),       # one group: two of four waves idle; residual in two passes
+    (2, 8, 2, 256, 1024, 8, 256),      # one group of G = 256; the largest residual window
+    (1, 3, 1, 512, 17, 4, 128),        # 3 q heads in a head block of 4
 ])
 def test_attention_parity_small(B, Hq, Hkv, Nq, R, m, G):
     print(f"attention B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} R={R} m={m} G={G}", flush=True)
