@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 D = 128
+COPY_CAL_BYTES = 1 << 30
+QUANT_SRC = os.path.join(ROOT, "kv_cache_calibration_amd", "csrc", "quantize_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_mfma_prefill_hbm_bytes.txt")
 
 
 def log(msg):
@@ -59,10 +62,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=32,
                     help="layers of the prefill workload (32 = the full workload)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB read + 1 GiB write elementwise kernel before the "
+                         "steps (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the quantizer shards by sequence with no exchange; see DESIGN.md)",
+              "(the quantizer shards by sequence with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -139,6 +145,15 @@ def main():
     torch.cuda.synchronize()
     log("decode caches ready")
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {COPY_CAL_BYTES} bytes read, {COPY_CAL_BYTES} bytes written")
+        del src, dst
+
     names = ["quantize", "attention", "append", "flush", "dequantize"]
     ev = {k: [] for k in names}
 
@@ -202,7 +217,7 @@ def main():
 
     roofline = {
         "bound": "hbm",
-        "kernel": "quantize_kernel (prefill launch)",
+        "kernel": "quantize_mfma_kernel (prefill launch)",
         "achieved": rates["quantize_gbps"],
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
@@ -211,6 +226,13 @@ def main():
         "bytes_per_launch": qb,
         "avg_launch_ms": ms["quantize"],
     }
+
+    tr = measured_traffic(QUANT_SRC, qb)
+    if tr is not None:
+        roofline["traffic"] = tr["bytes_per_launch"]              # HBM bytes per launch
+        roofline["traffic_unit"] = "bytes per launch"
+        roofline["traffic_gbps"] = tr["bytes_per_launch"] / (ms["quantize"] * 1e-3) / 1e9
+        roofline["traffic_detail"] = tr
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -243,6 +265,30 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(src_path, algorithmic_bytes):
+    """HBM bytes per launch of the dominant kernel, from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known size);
+    None when that summary was taken on another version of the kernel source
+    or for another launch size."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        with open(src_path, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("source_sha256", "").strip() != sha:
+            return None
+        if int(kv["algorithmic_bytes_per_launch"]) != int(algorithmic_bytes):
+            return None
+        return {"bytes_per_launch": float(kv["hbm_bytes_per_launch"]),
+                "read_bytes_per_launch": float(kv["read_bytes_per_launch"]),
+                "write_bytes_per_launch": float(kv["write_bytes_per_launch"]),
+                "ratio_to_algorithmic": float(kv["hbm_bytes_per_launch"]) / algorithmic_bytes,
+                "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
