@@ -120,6 +120,9 @@ __device__ __forceinline__ float wave_sum_fast(float x) {
 __device__ __forceinline__ float wave_max_fast(float x) {
   return wave_allreduce_dpp(x, [](float a, float b) { return fmaxf(a, b); });
 }
+__device__ __forceinline__ float wave_min_fast(float x) {
+  return wave_allreduce_dpp(x, [](float a, float b) { return fminf(a, b); });
+}
 // x(lane) + x(lane ^ 32) on the VALU (permlane32 swap of x with itself
 // yields the lower half in one result and the upper half in the other).
 __device__ __forceinline__ float half_pair_sum(float x) {

@@ -18,13 +18,13 @@
 //    the channel-major pass weighted by 1/s1 (exactly the pages' Shift, since
 //    the rotation is linear and orthonormal), z = y - o', s2 = ||z||/sqrt(d).
 // 3. Nearest codeword: the sub-vector's box in the 24^4 quantile grid gives
-//    up to eight candidate codes (one L2-resident u64); the first four are
-//    evaluated in place with the exact squared distance in fp32, lowest code
-//    first so ties keep the lowest index.  Sub-vectors whose box has five to
-//    eight candidates go to a per-wave LDS queue and are finished one per
-//    lane; boxes with more than eight and points off the grid are scanned over
-//    all codes by the whole wave.  Queue results are merged back with the
-//    same lexicographic (distance, code) order.
+//    up to eight candidate codes (one L2-resident u64), evaluated in place
+//    with the exact squared distance in fp32 in ascending code order, so
+//    ties keep the lowest index (the second four only when some lane of the
+//    wave has more than four).  Boxes with more than eight candidates and
+//    points off the grid are rare: the whole wave scans all 256 codes for
+//    them, one sub-vector at a time (broadcast by readlane, then a wave
+//    minimum of the distance and of the code among equal distances).
 // 4. Scale adjustment alpha = ||h||^2 / <h, h_hat>, codes, (s1, s2'), o'.
 #include "nsn_device.h"
 #include "nsn_launch.h"
@@ -38,19 +38,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kG = 128;
 constexpr int kNW = kG / 32;       // waves per workgroup
-constexpr int kQCap = 256;         // overflow queue entries per wave
 constexpr float kSqrtD = 11.313708498984761f;
-
-struct alignas(16) QEntry {
-  float h[4];
-  uint32_t codes;  // candidates five to eight (queue A)
-  uint32_t pad;
-  uint64_t res;    // lexicographic (distance, code) minimum, written back
-};
-
-__device__ __forceinline__ uint64_t dist_key(float d, uint32_t code) {
-  return (static_cast<uint64_t>(__float_as_uint(d)) << 32) | code;
-}
 
 __device__ __forceinline__ float sqdist4(const float* h, const float* c) {
   const float d0 = h[0] - c[0], d1 = h[1] - c[1], d2 = h[2] - c[2], d3 = h[3] - c[3];
@@ -69,7 +57,6 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   __shared__ float ascale[kG];
   __shared__ float csum[kNW][kD];
   __shared__ __attribute__((aligned(16))) float osh[kD];
-  __shared__ QEntry queue[kNW][kQCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -193,7 +180,6 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   //      candidate words of the next block are fetched while the current one
   //      is evaluated.
   const uint64_t* tmain = reinterpret_cast<const uint64_t*>(table + kTabMain);
-  QEntry* myq = queue[w];
   auto locate = [&](int mb, int q, bool& off) -> int {
     uint32_t bins[4];
 #pragma unroll
@@ -212,7 +198,6 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) wordv[0][q] = tmain[locate(0, q, offv[0][q])];
 
-  float bestd[16];
   uint32_t codes4[4] = {0u, 0u, 0u, 0u};   // best code of sub-vector k in byte k%4 of word k/4
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -221,108 +206,69 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) wordv[nxt][q] = tmain[locate(mb + 1, q, offv[nxt][q])];
     }
-    int na = 0, nb = 0;     // queue A (five to eight candidates), B (full scan)
-    int rank[4];
+    uint32_t scanmask = 0;   // bit q: sub-vector (mb, q) of this lane needs the full scan
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int k = 4 * mb + q;
       const float hv[4] = {acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
       const uint64_t wv = wordv[cur][q];
-      const uint32_t lo = static_cast<uint32_t>(wv);
+      const uint32_t lo = static_cast<uint32_t>(wv), hi = static_cast<uint32_t>(wv >> 32);
       const bool more4 = cand_more_than_4(wv);
       const bool scan = offv[cur][q] || cand_more_than_8(wv);
-      // the four lowest candidates in ascending code order, so a strict '<'
-      // keeps the lowest code among equal distances
+      // candidates in ascending code order, so a strict '<' keeps the lowest
+      // code among equal distances: the first four (byte-reversed when there
+      // are more than four), then bytes 4..7 (ascending, or repeats of the
+      // first four)
       const uint32_t asc = more4 ? __builtin_amdgcn_perm(0u, lo, 0x00010203u) : lo;
       float bd = __builtin_huge_valf();
       uint32_t bc = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t code = (asc >> (8 * i)) & 0xffu;
-        const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
-        const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-        const float d = sqdist4(hv, cv);
-        bc = d < bd ? code : bc;
-        bd = d < bd ? d : bd;
-      }
-      if (scan) bd = __builtin_huge_valf();   // the full scan decides
-      bestd[k] = bd;
-      codes4[mb] |= bc << (8 * q);
-      const bool qa = more4 && !scan;
-      const uint64_t ba = __ballot(qa), bb = __ballot(scan);
-      const uint64_t below = (uint64_t(1) << lane) - 1;
-      rank[q] = qa ? na + __popcll(ba & below) : (scan ? kQCap - 1 - (nb + __popcll(bb & below)) : -1);
-      if (qa || scan) {
-        QEntry e;
-        e.h[0] = hv[0];
-        e.h[1] = hv[1];
-        e.h[2] = hv[2];
-        e.h[3] = hv[3];
-        e.codes = static_cast<uint32_t>(wv >> 32);
-        e.pad = 0;
-        e.res = ~uint64_t(0);
-        myq[rank[q]] = e;
-      }
-      na += __popcll(ba);
-      nb += __popcll(bb);
-    }
-    if (na + nb > 0) {   // wave-uniform
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // A: one lane per entry, the four further candidates (ascending)
-      for (int qi = lane; qi < na; qi += kWave) {
-        const QEntry e = myq[qi];
-        uint64_t bk = ~uint64_t(0);
+      auto eval4 = [&](uint32_t word) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
+          const uint32_t code = (word >> (8 * i)) & 0xffu;
           const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
           const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-          const uint64_t key = dist_key(sqdist4(e.h, cv), code);
-          bk = key < bk ? key : bk;
+          const float d = sqdist4(hv, cv);
+          bc = d < bd ? code : bc;
+          bd = d < bd ? d : bd;
         }
-        myq[qi].res = bk;
-      }
-      // B: the whole wave scans all codes of one entry at a time
-      for (int bi = 0; bi < nb; ++bi) {
-        const int qi = kQCap - 1 - bi;
-        const float4 hq = *reinterpret_cast<const float4*>(myq[qi].h);
-        const float hv[4] = {hq.x, hq.y, hq.z, hq.w};
-        uint64_t bk = ~uint64_t(0);
-#pragma unroll
-        for (int r = 0; r < kCodes / kWave; ++r) {
-          const uint32_t code = static_cast<uint32_t>(lane + kWave * r);
-          const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
-          const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-          const uint64_t key = dist_key(sqdist4(hv, cv), code);
-          bk = key < bk ? key : bk;
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const uint64_t other = __shfl_xor(bk, o, kWave);
-          bk = other < bk ? other : bk;
-        }
-        if (lane == 0) myq[qi].res = bk;
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
+      eval4(asc);
+      if (__ballot(more4)) eval4(hi);   // wave-uniform
+      codes4[mb] |= bc << (8 * q);
+      scanmask |= scan ? (1u << q) : 0u;
+    }
+    // sub-vectors whose box has more than eight candidates or that lie off
+    // the grid: the whole wave scans all codes for one of them at a time
+    if (__ballot(scanmask != 0)) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (rank[q] >= 0) {
-          const uint64_t r = myq[rank[q]].res;
-          const float rd = __uint_as_float(static_cast<uint32_t>(r >> 32));
-          const uint32_t rc = static_cast<uint32_t>(r) & 0xffu;
-          const uint32_t oc = (codes4[mb] >> (8 * q)) & 0xffu;
-          const float od = bestd[4 * mb + q];
-          if (rd < od || (rd == od && rc < oc)) {
-            bestd[4 * mb + q] = rd;
-            codes4[mb] = (codes4[mb] & ~(0xffu << (8 * q))) | (rc << (8 * q));
+        uint64_t pend = __ballot((scanmask >> q) & 1u);
+        while (pend) {
+          const int src = __builtin_ctzll(pend);
+          pend &= pend - 1;
+          float hv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            hv[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[mb][4 * q + e]), src));
+          float bd = __builtin_huge_valf();
+          uint32_t bc = 0;
+#pragma unroll
+          for (int r = 0; r < kCodes / kWave; ++r) {
+            const uint32_t code = static_cast<uint32_t>(lane + kWave * r);
+            const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
+            const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
+            const float d = sqdist4(hv, cv);
+            bc = d < bd ? code : bc;
+            bd = d < bd ? d : bd;
+          }
+          const float dmin = wave_min_fast(bd);
+          const float cmin = wave_min_fast(bd == dmin ? static_cast<float>(bc) : 1e9f);
+          if (lane == src) {
+            const uint32_t c = static_cast<uint32_t>(cmin) & 0xffu;
+            codes4[mb] = (codes4[mb] & ~(0xffu << (8 * q))) | (c << (8 * q));
           }
         }
       }
-      __builtin_amdgcn_wave_barrier();
     }
   }
 
