@@ -45,6 +45,40 @@ __device__ __forceinline__ float sqdist4(const float* h, const float* c) {
   return fmaf(d3, d3, fmaf(d2, d2, fmaf(d1, d1, d0 * d0)));
 }
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// h - c for c the low (HI = 0) or high (HI = 1) fp16 half of w: one
+// v_fma_mix_f32 (h + (-1) c with c widened exactly), rounded like the fp32
+// subtraction.  Arithmetic only.
+template <int HI>
+__device__ __forceinline__ float sub_f16(float h, uint32_t w) {
+  float d;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(h));
+  else
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(h));
+  return d;
+}
+
+// Squared distance from h to codeword `code` of the fp16 codebook in LDS
+// (its entries are fp16 values, so this is the exact fp32 distance).
+__device__ __forceinline__ float sqdist_cb(const float (&h)[4], const uint32_t* cbh, uint32_t code) {
+  const uint2 w = *reinterpret_cast<const uint2*>(&cbh[2 * code]);
+  const float d0 = sub_f16<0>(h[0], w.x), d1 = sub_f16<1>(h[1], w.x);
+  const float d2 = sub_f16<0>(h[2], w.y), d3 = sub_f16<1>(h[3], w.y);
+  return fmaf(d3, d3, fmaf(d2, d2, fmaf(d1, d1, d0 * d0)));
+}
+
+// codeword `code` of the fp16 codebook in LDS, as fp32 (exact)
+__device__ __forceinline__ void codeword(const uint32_t* cbh, uint32_t code, float (&cv)[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(&cbh[2 * code]);
+  const h2v a = __builtin_bit_cast(h2v, w.x), b = __builtin_bit_cast(h2v, w.y);
+  cv[0] = static_cast<float>(a.x);
+  cv[1] = static_cast<float>(a.y);
+  cv[2] = static_cast<float>(b.x);
+  cv[3] = static_cast<float>(b.y);
+}
+
 __device__ __forceinline__ v8h as_v8h(u32x4 v) { return __builtin_bit_cast(v8h, v); }
 
 __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
@@ -52,11 +86,17 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
     const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
     uint16_t* __restrict__ meta, int64_t meta_seq_stride, uint16_t* __restrict__ shift,
     int64_t shift_seq_stride, int scale_adjust) {
-  __shared__ __attribute__((aligned(16))) float cb[kCodes * 4];
+  // fp16 codebook (the prepared codebook's entries are fp16 values, so this
+  // copy is exact and half the LDS traffic of fp32)
+  __shared__ __attribute__((aligned(16))) uint32_t cbh[kCodes * 2];
   __shared__ __attribute__((aligned(16))) uint8_t binlut[3 * kFine];   // sentinels around the grid
   __shared__ float ascale[kG];
   __shared__ float csum[kNW][kD];
   __shared__ __attribute__((aligned(16))) float osh[kD];
+  // per-wave staging of the wave's 32 input tokens: 16-byte chunk c of token
+  // t at slot 16 t + (c ^ (t % 16)), so both the coalesced writes and the
+  // operand-layout reads touch 16 different 4-bank groups per 16 lanes
+  __shared__ __attribute__((aligned(16))) u32x4 xs[kNW][32 * 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -67,8 +107,8 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   const int64_t tok = grp * kG + tg;
 
   {
-    const float* cbg = reinterpret_cast<const float*>(table + kTabCodebook);
-    for (int i = tid; i < kCodes * 4; i += kG * 2) cb[i] = cbg[i];
+    const uint32_t* cbg = reinterpret_cast<const uint32_t*>(table + kTabCodebookH);
+    for (int i = tid; i < kCodes * 2; i += kG * 2) cbh[i] = cbg[i];
     const uint32_t* bl = reinterpret_cast<const uint32_t*>(table + kTabBinLut);
     uint32_t* bd = reinterpret_cast<uint32_t*>(binlut);
     for (int i = tid; i < 3 * kFine / 4; i += kG * 2)
@@ -76,10 +116,26 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   }
 
   // ---- operands: x (fp16, 8 x 16 bytes per lane) and the H16 sign pattern
-  const __half* row = x + seq * x_seq_stride + tok * kD;
+  // the wave's 32 tokens are 8 KB of contiguous input: eight fully coalesced
+  // 1 KB loads, through LDS into the operand layout (lane (t, hf) needs the
+  // 16-byte chunks 2 kb + hf of token t)
   u32x4 xv[8];
+  {
+    const __half* wrow = x + seq * x_seq_stride + (grp * kG + 32 * w) * kD;
+    u32x4 ld[8];
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb) xv[kb] = load_nt16(row + 16 * kb + 8 * hf);
+    for (int i = 0; i < 8; ++i) ld[i] = load_nt16(wrow + 8 * (kWave * i + lane));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tt = 4 * i + (lane >> 4), c = lane & 15;
+      xs[w][16 * tt + (c ^ (tt & 15))] = ld[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) xv[kb] = xs[w][16 * t + ((2 * kb + hf) ^ (t & 15))];
+  }
   u32x4 P0, P1;
   {
     const int r16 = lane & 15, r4 = (lane >> 4) & 1;
@@ -225,9 +281,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t code = (word >> (8 * i)) & 0xffu;
-          const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
-          const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-          const float d = sqdist4(hv, cv);
+          const float d = sqdist_cb(hv, cbh, code);
           bc = d < bd ? code : bc;
           bd = d < bd ? d : bd;
         }
@@ -255,9 +309,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
           for (int r = 0; r < kCodes / kWave; ++r) {
             const uint32_t code = static_cast<uint32_t>(lane + kWave * r);
-            const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
-            const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
-            const float d = sqdist4(hv, cv);
+            const float d = sqdist_cb(hv, cbh, code);
             bc = d < bd ? code : bc;
             bd = d < bd ? d : bd;
           }
@@ -278,8 +330,8 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   for (int k = 0; k < 16; ++k) {
     const int mb = k >> 2, q = k & 3;
     const uint32_t code = (codes4[mb] >> (8 * q)) & 0xffu;
-    const float4 cw = *reinterpret_cast<const float4*>(&cb[4 * code]);
-    const float cv[4] = {cw.x, cw.y, cw.z, cw.w};
+    float cv[4];
+    codeword(cbh, code, cv);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       dot = fmaf(acc[mb][4 * q + e], cv[e], dot);
