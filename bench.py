@@ -139,7 +139,32 @@ def main():
         q = synth.query_torch((B3, Hq, D), seed=w3["seed"] + 10 * c + 1, device=dev)
         caches.append(((kc, km, ks), (vc, vm, vs), kr, vr, q))
         del K3, V3
-    ws_bytes = nsnq.nsn_decode_attention_workspace_size(p, B3, Hq, Hkv, Nq, R, Nq, R, scale)
+    # the same decode shape with 1-bit codes (m = 8): a side measurement,
+    # not part of the step
+    m1 = 8
+    p1 = nsnq.Params(sub_dim=m1, group_size=G)
+    X1 = torch.from_numpy(synth.codebook_samples(m1, 262144, seed=0)).to(dev)
+    cb1 = torch.empty((256, m1), dtype=torch.float32, device=dev)
+    cws1 = torch.empty(nsnq.nsn_build_codebook_workspace_size(m1, 262144), dtype=torch.uint8,
+                       device=dev)
+    nsnq.nsn_build_codebook(X1, cb1, cws1, iters=20)
+    table1 = torch.empty(nsnq.nsn_table_size(p1), dtype=torch.uint8, device=dev)
+    nsnq.nsn_prepare_codebook(p1, cb1, table1)
+    del X1, cws1
+    caches1 = []
+    for c in range(3):
+        K3, V3 = synth.kv_torch(B3 * Hkv, Nq + R, w3["outlier_scale"], w3["seed"] + 10 * c, dev)
+        kc = torch.empty((B3, Hkv, Nq, D // m1), dtype=torch.uint8, device=dev)
+        km = torch.empty((B3, Hkv, Nq, 2), dtype=torch.float16, device=dev)
+        ks = torch.empty((B3, Hkv, Nq // G, D), dtype=torch.float16, device=dev)
+        vc, vm, vs = torch.empty_like(kc), torch.empty_like(km), torch.empty_like(ks)
+        f = lambda t: t.view(B3 * Hkv, *t.shape[2:])  # noqa: E731
+        nsnq.nsn_quantize(p1, K3[:, :Nq], table1, f(kc), f(km), f(ks))
+        nsnq.nsn_quantize(p1, V3[:, :Nq], table1, f(vc), f(vm), f(vs))
+        caches1.append(((kc, km, ks), (vc, vm, vs), caches[c][2], caches[c][3], caches[c][4]))
+        del K3, V3
+    ws_bytes = max(nsnq.nsn_decode_attention_workspace_size(p, B3, Hq, Hkv, Nq, R, Nq, R, scale),
+                   nsnq.nsn_decode_attention_workspace_size(p1, B3, Hq, Hkv, Nq, R, Nq, R, scale))
     work = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B3, Hq, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -193,6 +218,24 @@ def main():
     wall = time.perf_counter() - t0
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in names}
     ms_step = wall * 1e3 / args.steps
+    launch_stats = {}
+    for k in names:
+        v = np.array([a.elapsed_time(b) for a, b in ev[k]])
+        launch_stats[k] = {"median_ms": float(np.median(v)), "p10_ms": float(np.percentile(v, 10)),
+                           "p90_ms": float(np.percentile(v, 90)), "n": int(len(v))}
+
+    # side measurement, outside the step: decode attention over 1-bit caches
+    ev1 = []
+    for i in range(max(args.steps, 3) + 1):
+        kc1, vc1, kr1, vr1, q1 = caches1[i % 3]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nsnq.nsn_decode_attention(p1, q1, kc1, vc1, kr1, vr1, table1, work, out, Nq, R, scale)
+        b.record(stream)
+        if i > 0:
+            ev1.append((a, b))
+    torch.cuda.synchronize()
+    ms_attn1 = float(np.mean([a.elapsed_time(b) for a, b in ev1]))
 
     qb = quant_bytes(n_seq, T, m, G)
     ab = attn_bytes(B3, Hq, Hkv, Nq, R, m, G)
@@ -206,12 +249,15 @@ def main():
         "quantize_fp16_in_gbps": n_seq * T * D * 2 / (ms["quantize"] * 1e-3) / 1e9,
         "quantize_token_heads_per_s": n_seq * T / (ms["quantize"] * 1e-3),
         "attention_gbps": ab / (ms["attention"] * 1e-3) / 1e9,
+        "attention_1bit_gbps": attn_bytes(B3, Hq, Hkv, Nq, R, m1, G) / (ms_attn1 * 1e-3) / 1e9,
+        "attention_1bit_ms": ms_attn1,
         "attention_query_tokens_per_s": B3 / (ms["attention"] * 1e-3),
         "flush_gbps": fb / (ms["flush"] * 1e-3) / 1e9,
         "dequantize_gbps": db / (ms["dequantize"] * 1e-3) / 1e9,
     }
     rates["quantize_frac_hbm"] = rates["quantize_gbps"] / HBM_PEAK_GBPS
     rates["attention_frac_hbm"] = rates["attention_gbps"] / HBM_PEAK_GBPS
+    rates["attention_1bit_frac_hbm"] = rates["attention_1bit_gbps"] / HBM_PEAK_GBPS
     log("kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ms.items()))
     log("rates: " + ", ".join(f"{k} {v:.4g}" for k, v in rates.items()))
 
@@ -259,12 +305,29 @@ def main():
             "step_bytes": step_bytes,
         },
         "kernel_ms": ms,
+        "launch_stats": launch_stats,
+        "gpu_clocks": gpu_clocks(),
         "rates": rates,
         "codebook_build_ms": codebook_ms,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def gpu_clocks():
+    """Current clock levels as rocm-smi reports them (best effort)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    try:
+        r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    lines = [ln.strip() for ln in r.stdout.splitlines() if "Mhz" in ln or "MHz" in ln]
+    return lines[:8] or None
 
 
 def measured_traffic(src_path, algorithmic_bytes):
