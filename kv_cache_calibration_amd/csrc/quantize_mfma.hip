@@ -45,6 +45,20 @@ __device__ __forceinline__ float sqdist4(const float* h, const float* c) {
   return fmaf(d3, d3, fmaf(d2, d2, fmaf(d1, d1, d0 * d0)));
 }
 
+struct alignas(16) QEntry {
+  float h[4];
+  uint32_t codes;  // candidates five to eight, ascending
+  float best;      // best distance among the first four
+  uint32_t dst;    // byte of the owner's result row
+  uint32_t pad;
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 // h - c for c the low (HI = 0) or high (HI = 1) fp16 half of w: one
@@ -97,6 +111,8 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   // t at slot 16 t + (c ^ (t % 16)), so both the coalesced writes and the
   // operand-layout reads touch 16 different 4-bank groups per 16 lanes
   __shared__ __attribute__((aligned(16))) u32x4 xs[kNW][32 * 16];
+  // per-lane result row (16 code bytes) that queued sub-vectors update
+  __shared__ __attribute__((aligned(16))) uint32_t res[kNW][kWave][4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -255,6 +271,13 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   for (int q = 0; q < 4; ++q) wordv[0][q] = tmain[locate(0, q, offv[0][q])];
 
   uint32_t codes4[4] = {0u, 0u, 0u, 0u};   // best code of sub-vector k in byte k%4 of word k/4
+  // Boxes with five to eight candidates: the first four are evaluated in
+  // place; the sub-vector, its other four candidates and its best distance
+  // so far go to a per-wave queue (in the staging tile, free by now), which
+  // the wave then works through one entry per lane, writing an improved code
+  // straight into the owner's result row.
+  QEntry* myq = reinterpret_cast<QEntry*>(&xs[w][0]);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int cur = mb & 1, nxt = cur ^ 1;
@@ -263,6 +286,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       for (int q = 0; q < 4; ++q) wordv[nxt][q] = tmain[locate(mb + 1, q, offv[nxt][q])];
     }
     uint32_t scanmask = 0;   // bit q: sub-vector (mb, q) of this lane needs the full scan
+    int nq = 0;              // queue entries of this step (wave-uniform)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float hv[4] = {acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
@@ -270,26 +294,36 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       const uint32_t lo = static_cast<uint32_t>(wv), hi = static_cast<uint32_t>(wv >> 32);
       const bool more4 = cand_more_than_4(wv);
       const bool scan = offv[cur][q] || cand_more_than_8(wv);
-      // candidates in ascending code order, so a strict '<' keeps the lowest
-      // code among equal distances: the first four (byte-reversed when there
-      // are more than four), then bytes 4..7 (ascending, or repeats of the
-      // first four)
+      // the four lowest candidates in ascending code order (byte-reversed
+      // when there are more than four), so a strict '<' keeps the lowest code
+      // among equal distances
       const uint32_t asc = more4 ? __builtin_amdgcn_perm(0u, lo, 0x00010203u) : lo;
       float bd = __builtin_huge_valf();
       uint32_t bc = 0;
-      auto eval4 = [&](uint32_t word) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t code = (word >> (8 * i)) & 0xffu;
-          const float d = sqdist_cb(hv, cbh, code);
-          bc = d < bd ? code : bc;
-          bd = d < bd ? d : bd;
-        }
-      };
-      eval4(asc);
-      if (__ballot(more4)) eval4(hi);   // wave-uniform
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = (asc >> (8 * i)) & 0xffu;
+        const float d = sqdist_cb(hv, cbh, code);
+        bc = d < bd ? code : bc;
+        bd = d < bd ? d : bd;
+      }
       codes4[mb] |= bc << (8 * q);
       scanmask |= scan ? (1u << q) : 0u;
+      const bool enq = more4 && !scan;
+      const uint64_t bq = __ballot(enq);
+      if (enq) {
+        QEntry e;
+        e.h[0] = hv[0];
+        e.h[1] = hv[1];
+        e.h[2] = hv[2];
+        e.h[3] = hv[3];
+        e.codes = hi;
+        e.best = bd;
+        e.dst = static_cast<uint32_t>(lane * 16 + 4 * mb + q);
+        e.pad = 0;
+        myq[nq + __popcll(bq & below)] = e;
+      }
+      nq += __popcll(bq);
     }
     // sub-vectors whose box has more than eight candidates or that lie off
     // the grid: the whole wave scans all codes for one of them at a time
@@ -322,6 +356,33 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
         }
       }
     }
+    res[w][lane][mb] = codes4[mb];
+    if (nq > 0) {
+      wave_lds_sync();
+      // candidates five to eight are ascending and above the first four, so
+      // a strict '<' against the best so far keeps the lowest code on ties
+      for (int qi = lane; qi < nq; qi += kWave) {
+        const QEntry e = myq[qi];
+        float bd = e.best;
+        uint32_t bc = 0xffffffffu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
+          const float d = sqdist_cb(e.h, cbh, code);
+          bc = d < bd ? code : bc;
+          bd = d < bd ? d : bd;
+        }
+        if (bc != 0xffffffffu) reinterpret_cast<uint8_t*>(&res[w][0][0])[e.dst] = static_cast<uint8_t>(bc);
+      }
+      wave_lds_sync();
+    }
+  }
+  {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(&res[w][lane][0]);
+    codes4[0] = r.x;
+    codes4[1] = r.y;
+    codes4[2] = r.z;
+    codes4[3] = r.w;
   }
 
   // ---- scale adjustment, codes, metadata
