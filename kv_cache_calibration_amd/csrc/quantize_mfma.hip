@@ -17,6 +17,8 @@
 // 2. NSN in the rotated domain: s1 from the token norm, the group mean from
 //    the channel-major pass weighted by 1/s1 (exactly the pages' Shift, since
 //    the rotation is linear and orthonormal), z = y - o', s2 = ||z||/sqrt(d).
+//    h = z / s2 is never formed: the search compares ||z - s2 c||^2, which
+//    orders the codewords as ||h - c||^2 does.
 // 3. Nearest codeword: the sub-vector's box in the 24^4 quantile grid gives
 //    up to eight candidate codes (one L2-resident u64), evaluated in place
 //    with the exact squared distance in fp32 in ascending code order, so
@@ -40,17 +42,12 @@ constexpr int kG = 128;
 constexpr int kNW = kG / 32;       // waves per workgroup
 constexpr float kSqrtD = 11.313708498984761f;
 
-__device__ __forceinline__ float sqdist4(const float* h, const float* c) {
-  const float d0 = h[0] - c[0], d1 = h[1] - c[1], d2 = h[2] - c[2], d3 = h[3] - c[3];
-  return fmaf(d3, d3, fmaf(d2, d2, fmaf(d1, d1, d0 * d0)));
-}
-
 struct alignas(16) QEntry {
   float h[4];
   uint32_t codes;  // candidates five to eight, ascending
   float best;      // best distance among the first four
   uint32_t dst;    // byte of the owner's result row
-  uint32_t pad;
+  float ns;        // -s2 of the owner's token
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -64,22 +61,26 @@ typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 // h - c for c the low (HI = 0) or high (HI = 1) fp16 half of w: one
 // v_fma_mix_f32 (h + (-1) c with c widened exactly), rounded like the fp32
 // subtraction.  Arithmetic only.
+// z + ns c for c the low (HI = 0) or high (HI = 1) fp16 half of w: one
+// v_fma_mix_f32 (c widened exactly).  Arithmetic only.
 template <int HI>
-__device__ __forceinline__ float sub_f16(float h, uint32_t w) {
+__device__ __forceinline__ float fma_f16(uint32_t w, float ns, float z) {
   float d;
   if constexpr (HI)
-    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(h));
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(ns), "v"(z));
   else
-    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(h));
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(ns), "v"(z));
   return d;
 }
 
-// Squared distance from h to codeword `code` of the fp16 codebook in LDS
-// (its entries are fp16 values, so this is the exact fp32 distance).
-__device__ __forceinline__ float sqdist_cb(const float (&h)[4], const uint32_t* cbh, uint32_t code) {
+// ||z - s c||^2 for codeword `code` of the fp16 codebook in LDS, ns = -s.
+// With z = s h this is s^2 ||h - c||^2: the same order over codewords as the
+// distance to h, without forming h.
+__device__ __forceinline__ float sqdist_cb(const float (&z)[4], const uint32_t* cbh, uint32_t code,
+                                           float ns) {
   const uint2 w = *reinterpret_cast<const uint2*>(&cbh[2 * code]);
-  const float d0 = sub_f16<0>(h[0], w.x), d1 = sub_f16<1>(h[1], w.x);
-  const float d2 = sub_f16<0>(h[2], w.y), d3 = sub_f16<1>(h[3], w.y);
+  const float d0 = fma_f16<0>(w.x, ns, z[0]), d1 = fma_f16<1>(w.x, ns, z[1]);
+  const float d2 = fma_f16<0>(w.y, ns, z[2]), d3 = fma_f16<1>(w.y, ns, z[3]);
   return fmaf(d3, d3, fmaf(d2, d2, fmaf(d1, d1, d0 * d0)));
 }
 
@@ -242,11 +243,11 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
     }
   ss2 = half_pair_sum(ss2);
   const float s2 = sqrtf(ss2 * (1.0f / kD));
-  const float inv2 = s2 > 0.f ? 1.0f / s2 : 0.f;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mb][r] *= inv2;   // h
+  // The search runs on z = s2 h directly: distances ||z - s2 c||^2 and bins
+  // of z / s2.  A zero z (s2 = 0) is h = 0: scale 1 gives the same answer.
+  const float sc = s2 > 0.f ? s2 : 1.0f;
+  const float nsc = -sc;
+  const float fine_scale = kFineInv / sc;
 
   // ---- nearest codeword, four sub-vectors (one mb block) per step; the
   //      candidate words of the next block are fetched while the current one
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
     for (int e = 0; e < 4; ++e) {
       // fine index + 1024; off-grid and non-finite values land on sentinels
       const uint32_t fi = static_cast<uint32_t>(
-          static_cast<int>(fmaf(acc[mb][4 * q + e], kFineInv, 512.0f + kFine)));
+          static_cast<int>(fmaf(acc[mb][4 * q + e], fine_scale, 512.0f + kFine)));
       bins[e] = binlut[min(fi, static_cast<uint32_t>(3 * kFine - 1))];
     }
     off = ((bins[0] | bins[1] | bins[2] | bins[3]) & 0x80u) != 0;
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t code = (asc >> (8 * i)) & 0xffu;
-        const float d = sqdist_cb(hv, cbh, code);
+        const float d = sqdist_cb(hv, cbh, code, nsc);
         bc = d < bd ? code : bc;
         bd = d < bd ? d : bd;
       }
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
         e.codes = hi;
         e.best = bd;
         e.dst = static_cast<uint32_t>(lane * 16 + 4 * mb + q);
-        e.pad = 0;
+        e.ns = nsc;
         myq[nq + __popcll(bq & below)] = e;
       }
       nq += __popcll(bq);
@@ -338,12 +339,13 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             hv[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[mb][4 * q + e]), src));
+          const float ns = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nsc), src));
           float bd = __builtin_huge_valf();
           uint32_t bc = 0;
 #pragma unroll
           for (int r = 0; r < kCodes / kWave; ++r) {
             const uint32_t code = static_cast<uint32_t>(lane + kWave * r);
-            const float d = sqdist_cb(hv, cbh, code);
+            const float d = sqdist_cb(hv, cbh, code, ns);
             bc = d < bd ? code : bc;
             bd = d < bd ? d : bd;
           }
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
-          const float d = sqdist_cb(e.h, cbh, code);
+          const float d = sqdist_cb(e.h, cbh, code, e.ns);
           bc = d < bd ? code : bc;
           bd = d < bd ? d : bd;
         }
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   }
 
   // ---- scale adjustment, codes, metadata
-  float dot = 0.f, hh = 0.f;
+  float dot = 0.f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int mb = k >> 2, q = k & 3;
@@ -396,12 +398,11 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       dot = fmaf(acc[mb][4 * q + e], cv[e], dot);
-      hh = fmaf(acc[mb][4 * q + e], acc[mb][4 * q + e], hh);
     }
   }
+  // <h, h_hat> = <z, h_hat> / s2 and ||h||^2 = d exactly (Normalize #2)
   dot = half_pair_sum(dot);
-  hh = half_pair_sum(hh);
-  const float alpha = (scale_adjust && dot > 0.f) ? hh / dot : 1.0f;
+  const float alpha = (scale_adjust && dot > 0.f) ? (kD * s2) / dot : 1.0f;
   const uint32_t own[4] = {codes4[0], codes4[1], codes4[2], codes4[3]};
 
   // Lane half 0 holds the even sub-vectors, half 1 the odd ones.  After the
