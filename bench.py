@@ -319,11 +319,16 @@ def gpu_clocks():
     """Current clock levels as rocm-smi reports them (best effort)."""
     import shutil
     import subprocess
+    if "rocprofiler" in os.environ.get("LD_PRELOAD", "") or any(
+            k.startswith("ROCPROF") for k in os.environ):
+        return None   # under a profiler: no child processes
     exe = shutil.which("rocm-smi")
     if exe is None:
         return None
     try:
-        r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=20)
+        # run the script with this interpreter (no /usr/bin/env hop)
+        r = subprocess.run([sys.executable, os.path.realpath(exe), "--showclocks"],
+                           capture_output=True, text=True, timeout=20)
     except (OSError, subprocess.SubprocessError):
         return None
     lines = [ln.strip() for ln in r.stdout.splitlines() if "Mhz" in ln or "MHz" in ln]
