@@ -95,8 +95,7 @@ struct SplitSmem {
   float wl[kWaves][kHB];
 };
 struct ResidSmem {
-  float4 sres[kMaxResid];          // per token: scores, then weights, of the 4 heads
-  float red[kWaves][kHB];
+  float4 sres[kMaxResid];          // per token: scores of the 4 heads (base 2)
   float vpart[kWaves][kHB][kD];
 };
 template <int M>
@@ -225,10 +224,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // The fp16 residual window of one (batch, kv head, head block), in the
-// original domain, written as partial n_split.  Scores: fp16 q and k are
-// exact MFMA inputs (fp32 sums); values: one thread per (channel pair,
-// token quarter), the quarters summed through LDS.
+// original domain, written as partial n_split.  Every load is issued first;
+// scores are exact MFMA products of the fp16 q and k (fp32 sums) into LDS;
+// after one barrier every wave takes the per-head max and sum itself; values
+// run one thread per (channel pair, token residue mod 4) with weights formed
+// on the fly, and the four residue classes are summed through LDS.
 __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh, int hb) {
+  constexpr int kVPre = 32;              // value words held in registers per thread
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -237,11 +239,18 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
   const int nh = min(kHB, p.grp - hb * kHB);
   const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;
   const uint16_t* krow = p.kr + row * p.rcap * kD;
-  const uint16_t* vrow = p.vr + row * p.rcap * kD;
+  const uint32_t* vrow = reinterpret_cast<const uint32_t*>(p.vr + row * p.rcap * kD);
   const int nr = p.n_resid;
   const float qscale = p.scale * kLog2e;   // scores in base-2 units
   const float ninf = -__builtin_huge_valf();
 
+  // ---- all loads: this thread's value words, the wave's key blocks, q
+  uint32_t vpre[kVPre];
+#pragma unroll
+  for (int i = 0; i < kVPre; ++i) {
+    const int t = wave + kWaves * i;
+    vpre[i] = t < nr ? vrow[static_cast<int64_t>(t) * (kD / 2) + lane] : 0u;
+  }
   // A operand per step s: row c16 = head c16 (< nh), K index 8R + v =
   // channel 32 s + 8R + v
   u32x4 qa[4];
@@ -250,12 +259,11 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
     qa[s] = c16 < nh ? *reinterpret_cast<const u32x4*>(
                            p.q + (static_cast<int64_t>(b) * p.Hq + h0 + c16) * kD + 32 * s + 8 * R)
                      : u32x4{0u, 0u, 0u, 0u};
-  // two 16-token blocks per wave and pass, all loads issued first
-  for (int tb = 2 * wave; tb * 16 < nr; tb += 2 * kWaves) {
+  for (int tb0 = 2 * wave; tb0 * 16 < nr; tb0 += 2 * kWaves) {
     u32x4 kb[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int t = (tb + u) * 16 + c16;
+      const int t = (tb0 + u) * 16 + c16;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         kb[u][s] = t < nr ? *reinterpret_cast<const u32x4*>(krow + static_cast<int64_t>(t) * kD + 32 * s + 8 * R)
@@ -263,7 +271,7 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int t = (tb + u) * 16 + c16;
+      const int t = (tb0 + u) * 16 + c16;
       v4f d = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) d = mfma16(qa[s], kb[u][s], d);
@@ -272,64 +280,47 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
     }
   }
   __syncthreads();
-  float mx[kHB] = {ninf, ninf, ninf, ninf};
-  for (int t = tid; t < nr; t += kThreads) {
+  // ---- per-head max and sum, every wave over all tokens
+  float mres[kHB] = {ninf, ninf, ninf, ninf};
+  for (int t = lane; t < nr; t += kWave) {
     const float4 v = sm.sres[t];
-    mx[0] = fmaxf(mx[0], v.x);
-    mx[1] = fmaxf(mx[1], v.y);
-    mx[2] = fmaxf(mx[2], v.z);
-    mx[3] = fmaxf(mx[3], v.w);
+    mres[0] = fmaxf(mres[0], v.x);
+    mres[1] = fmaxf(mres[1], v.y);
+    mres[2] = fmaxf(mres[2], v.z);
+    mres[3] = fmaxf(mres[3], v.w);
   }
 #pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    mx[h] = wave_max_fast(mx[h]);
-    if (lane == 0) sm.red[wave][h] = mx[h];
-  }
-  __syncthreads();
-  float mres[kHB];
-#pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    float m = sm.red[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, sm.red[w][h]);
-    mres[h] = m;
-  }
-  __syncthreads();
-  float ls[kHB] = {0.f, 0.f, 0.f, 0.f};
-  for (int t = tid; t < nr; t += kThreads) {
-    float4 v = sm.sres[t];
-    v.x = exp2_fast(v.x - mres[0]);
-    v.y = exp2_fast(v.y - mres[1]);
-    v.z = exp2_fast(v.z - mres[2]);
-    v.w = exp2_fast(v.w - mres[3]);
-    sm.sres[t] = v;
-    ls[0] += v.x;
-    ls[1] += v.y;
-    ls[2] += v.z;
-    ls[3] += v.w;
+  for (int h = 0; h < kHB; ++h) mres[h] = wave_max_fast(mres[h]);
+  float lres[kHB] = {0.f, 0.f, 0.f, 0.f};
+  for (int t = lane; t < nr; t += kWave) {
+    const float4 v = sm.sres[t];
+    lres[0] += exp2_fast(v.x - mres[0]);
+    lres[1] += exp2_fast(v.y - mres[1]);
+    lres[2] += exp2_fast(v.z - mres[2]);
+    lres[3] += exp2_fast(v.w - mres[3]);
   }
 #pragma unroll
-  for (int h = 0; h < kHB; ++h) {
-    ls[h] = wave_sum_fast(ls[h]);
-    if (lane == 0) sm.red[wave][h] = ls[h];
-  }
-  __syncthreads();
-  // values: this thread's channels 2 lane, 2 lane + 1 over tokens wave, wave + 4, ...
+  for (int h = 0; h < kHB; ++h) lres[h] = wave_sum_fast(lres[h]);
+  // ---- values: channels 2 lane, 2 lane + 1; tokens wave, wave + 4, ...
   float a[kHB][2] = {};
-#pragma unroll 16
-  for (int t = wave; t < nr; t += kWaves) {
-    const uint32_t v = reinterpret_cast<const uint32_t*>(vrow + static_cast<int64_t>(t) * kD)[lane];
+  auto accumulate = [&](int t, uint32_t v) {
     const float v0 = h2f(v & 0xffffu), v1 = h2f(v >> 16);
-    const float4 pv = sm.sres[t];
-    a[0][0] = fmaf(pv.x, v0, a[0][0]);
-    a[0][1] = fmaf(pv.x, v1, a[0][1]);
-    a[1][0] = fmaf(pv.y, v0, a[1][0]);
-    a[1][1] = fmaf(pv.y, v1, a[1][1]);
-    a[2][0] = fmaf(pv.z, v0, a[2][0]);
-    a[2][1] = fmaf(pv.z, v1, a[2][1]);
-    a[3][0] = fmaf(pv.w, v0, a[3][0]);
-    a[3][1] = fmaf(pv.w, v1, a[3][1]);
+    const float4 sv = sm.sres[t];
+    const float pw[kHB] = {exp2_fast(sv.x - mres[0]), exp2_fast(sv.y - mres[1]),
+                           exp2_fast(sv.z - mres[2]), exp2_fast(sv.w - mres[3])};
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      a[h][0] = fmaf(pw[h], v0, a[h][0]);
+      a[h][1] = fmaf(pw[h], v1, a[h][1]);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kVPre; ++i) {
+    const int t = wave + kWaves * i;
+    if (t < nr) accumulate(t, vpre[i]);
   }
+  for (int t = wave + kWaves * kVPre; t < nr; t += kWaves)
+    accumulate(t, vrow[static_cast<int64_t>(t) * (kD / 2) + lane]);
 #pragma unroll
   for (int h = 0; h < kHB; ++h)
     *reinterpret_cast<float2*>(&sm.vpart[wave][h][2 * lane]) = make_float2(a[h][0], a[h][1]);
@@ -341,18 +332,18 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) acc += sm.vpart[w][h][c];
-    float mh = mres[0];
+    float mh = mres[0], lh = lres[0];
 #pragma unroll
-    for (int kk = 1; kk < kHB; ++kk) mh = h == kk ? mres[kk] : mh;
+    for (int kk = 1; kk < kHB; ++kk) {
+      mh = h == kk ? mres[kk] : mh;
+      lh = h == kk ? lres[kk] : lh;
+    }
     if (h < nh) {
       float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * (p.n_split + 1) + p.n_split) * kPartStride;
       dst[c] = acc;
       if (c == 0) {
-        float l = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) l += sm.red[w][h];
         dst[128] = mh;
-        dst[129] = l;
+        dst[129] = lh;
       }
     }
   }
