@@ -48,6 +48,13 @@ __device__ __forceinline__ bool cand_more_than_4(uint64_t w) {
 __device__ __forceinline__ bool cand_more_than_8(uint64_t w) {
   return ((w >> 32) & 0xffu) > ((w >> 40) & 0xffu);
 }
+// The same tests on the low (b0..b3) and high (b4..b7) 32-bit halves.
+__device__ __forceinline__ bool cand_more_than_4_lo(uint32_t lo) {
+  return (lo & 0xffu) > ((lo >> 8) & 0xffu);
+}
+__device__ __forceinline__ bool cand_more_than_8_hi(uint32_t hi) {
+  return (hi & 0xffu) > ((hi >> 8) & 0xffu);
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -293,8 +293,8 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       const float hv[4] = {acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
       const uint64_t wv = wordv[cur][q];
       const uint32_t lo = static_cast<uint32_t>(wv), hi = static_cast<uint32_t>(wv >> 32);
-      const bool more4 = cand_more_than_4(wv);
-      const bool scan = offv[cur][q] || cand_more_than_8(wv);
+      const bool more4 = cand_more_than_4_lo(lo);
+      const bool scan = offv[cur][q] || cand_more_than_8_hi(hi);
       // the four lowest candidates in ascending code order (byte-reversed
       // when there are more than four), so a strict '<' keeps the lowest code
       // among equal distances
