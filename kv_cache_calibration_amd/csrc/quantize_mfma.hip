@@ -1,5 +1,6 @@
-// Quantize for fp16 input, 2-bit codes (m = 4) and groups of 128 tokens, on
-// the matrix cores and the certified candidate tables.
+// Quantize for fp16 input and groups of 128 tokens on the matrix cores:
+// 2-bit codes (m = 4) through certified candidate tables, 1-bit codes (m = 8)
+// through an exhaustive matrix-core search.
 // [NSNQuant summary (gist.science), Methodology §1 NSN, §2 Hadamard
 //  rotation, §3 nearest codeword in one global codebook, scale adjustment.]
 //
@@ -11,22 +12,33 @@
 //    that depends only on the block and on bit 4 of the row; the +-1 entries
 //    and the fp16 input are exact, and v_mfma_f32_32x32x16_f16 accumulates in
 //    fp32.  Token-major pass: D[c][t] = (H x_t)[c] -- lane (t, half) gets the
-//    channels {32mb + 8q + 4half + e}, i.e. sub-vectors j = 8mb + 2q + half,
-//    each as four consecutive registers.  Channel-major pass (same operand
-//    registers, roles swapped): D[t][c], used for the per-channel group sums.
+//    channels {32mb + 8q + 4half + e}: for m = 4 the sub-vectors
+//    j = 8mb + 2q + half, each as four consecutive registers; for m = 8 half
+//    of sub-vector j = 4mb + q.  Channel-major pass (same operand registers,
+//    roles swapped): D[t][c], used for the per-channel group sums.
 // 2. NSN in the rotated domain: s1 from the token norm, the group mean from
 //    the channel-major pass weighted by 1/s1 (exactly the pages' Shift, since
 //    the rotation is linear and orthonormal), z = y - o', s2 = ||z||/sqrt(d).
-//    h = z / s2 is never formed: the search compares ||z - s2 c||^2, which
-//    orders the codewords as ||h - c||^2 does.
-// 3. Nearest codeword: the sub-vector's box in the 24^4 quantile grid gives
-//    up to eight candidate codes (one L2-resident u64), evaluated in place
-//    with the exact squared distance in fp32 in ascending code order, so
-//    ties keep the lowest index (the second four only when some lane of the
-//    wave has more than four).  Boxes with more than eight candidates and
-//    points off the grid are rare: the whole wave scans all 256 codes for
-//    them, one sub-vector at a time (broadcast by readlane, then a wave
-//    minimum of the distance and of the code among equal distances).
+// 3a. Nearest codeword, m = 4: h = z / s2 is never formed: the search
+//    compares ||z - s2 c||^2, which orders the codewords as ||h - c||^2 does.
+//    The sub-vector's box in the 24^4 quantile grid gives up to eight
+//    candidate codes (one L2-resident u64), evaluated in place with the exact
+//    squared distance in fp32 in ascending code order, so ties keep the
+//    lowest index (the second four only when some lane of the wave has more
+//    than four).  Boxes with more than eight candidates and points off the
+//    grid are rare: the whole wave scans all 256 codes for them, one
+//    sub-vector at a time (broadcast by readlane, then a wave minimum of the
+//    distance and of the code among equal distances).
+// 3b. Nearest codeword, m = 8: for each sub-vector index j the wave forms
+//    D[c][t] = ||c||^2 + H_t - 2 <c, h_t> for all 256 codes c and its 32
+//    tokens t with two MFMAs per 32-code tile.  h enters as an fp16 pair
+//    (hi + lo, 22 significant bits), the codebook is exact in fp16, ||c||^2
+//    as an fp16 pair, and H_t >= ||h_t||^2 (rounded up) keeps every value
+//    non-negative.  Each lane then takes the minimum of its 16 values per
+//    tile with the row number in the four low mantissa bits (a key that
+//    orders like the distance to within 15 ulp, ties to the lowest code),
+//    keeps the best tile, and the two lane halves of a token settle the
+//    final code.
 // 4. Scale adjustment alpha = ||h||^2 / <h, h_hat>, codes, (s1, s2'), o'.
 #include "nsn_device.h"
 #include "nsn_launch.h"
@@ -96,41 +108,28 @@ __device__ __forceinline__ void codeword(const uint32_t* cbh, uint32_t code, flo
 
 __device__ __forceinline__ v8h as_v8h(u32x4 v) { return __builtin_bit_cast(v8h, v); }
 
-__global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
-    const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
-    const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
-    uint16_t* __restrict__ meta, int64_t meta_seq_stride, uint16_t* __restrict__ shift,
-    int64_t shift_seq_stride, int scale_adjust) {
-  // fp16 codebook (the prepared codebook's entries are fp16 values, so this
-  // copy is exact and half the LDS traffic of fp32)
-  __shared__ __attribute__((aligned(16))) uint32_t cbh[kCodes * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t binlut[3 * kFine];   // sentinels around the grid
-  __shared__ float ascale[kG];
-  __shared__ float csum[kNW][kD];
-  __shared__ __attribute__((aligned(16))) float osh[kD];
+// Shared memory of the front end (steps 1 and 2).
+struct FrontSmem {
+  float ascale[kG];
+  float csum[kNW][kD];
+  __attribute__((aligned(16))) float osh[kD];
   // per-wave staging of the wave's 32 input tokens: 16-byte chunk c of token
   // t at slot 16 t + (c ^ (t % 16)), so both the coalesced writes and the
   // operand-layout reads touch 16 different 4-bank groups per 16 lanes
-  __shared__ __attribute__((aligned(16))) u32x4 xs[kNW][32 * 16];
-  // per-lane result row (16 code bytes) that queued sub-vectors update
-  __shared__ __attribute__((aligned(16))) uint32_t res[kNW][kWave][4];
+  __attribute__((aligned(16))) u32x4 xs[kNW][32 * 16];
+};
 
+// Steps 1 and 2 for the group (seq, grp).  On return acc[mb][4q + e] holds z
+// of channel 32mb + 8q + 4hf + e of the lane's token; fs.osh holds the group's
+// rotated shift o'.  Contains block barriers: every thread of the workgroup
+// calls it.
+__device__ __forceinline__ void nsn_front(const __half* __restrict__ x, int64_t x_seq_stride,
+                                          int64_t seq, int64_t grp, FrontSmem& fs,
+                                          v16f (&acc)[4], float& s1, float& s2) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int t = lane & 31, hf = lane >> 5;
-  const int64_t seq = blockIdx.x / n_groups;
-  const int64_t grp = blockIdx.x - seq * n_groups;
   const int tg = 32 * w + t;                          // token within the group
-  const int64_t tok = grp * kG + tg;
-
-  {
-    const uint32_t* cbg = reinterpret_cast<const uint32_t*>(table + kTabCodebookH);
-    for (int i = tid; i < kCodes * 2; i += kG * 2) cbh[i] = cbg[i];
-    const uint32_t* bl = reinterpret_cast<const uint32_t*>(table + kTabBinLut);
-    uint32_t* bd = reinterpret_cast<uint32_t*>(binlut);
-    for (int i = tid; i < 3 * kFine / 4; i += kG * 2)
-      bd[i] = (i >= kFine / 4 && i < 2 * kFine / 4) ? bl[i - kFine / 4] : 0x80808080u;
-  }
 
   // ---- operands: x (fp16, 8 x 16 bytes per lane) and the H16 sign pattern
   // the wave's 32 tokens are 8 KB of contiguous input: eight fully coalesced
@@ -145,13 +144,13 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tt = 4 * i + (lane >> 4), c = lane & 15;
-      xs[w][16 * tt + (c ^ (tt & 15))] = ld[i];
+      fs.xs[w][16 * tt + (c ^ (tt & 15))] = ld[i];
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) xv[kb] = xs[w][16 * t + ((2 * kb + hf) ^ (t & 15))];
+    for (int kb = 0; kb < 8; ++kb) xv[kb] = fs.xs[w][16 * t + ((2 * kb + hf) ^ (t & 15))];
   }
   u32x4 P0, P1;
   {
@@ -173,7 +172,6 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #define HBLK(a, kb) as_v8h((__popc((2 * (a)) & (kb)) & 1) ? (((kb) & 1) ? N1 : N0) : (((kb) & 1) ? P1 : P0))
 
   // ---- token-major rotation: acc[mb][r] = (H x_t)[32mb + 8(r/4) + 4hf + r%4]
-  v16f acc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = v16f{};
 #pragma unroll
@@ -190,9 +188,9 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
     for (int r = 0; r < 16; ++r) ss = fmaf(acc[mb][r], acc[mb][r], ss);
   ss = half_pair_sum(ss);
   const float nrm = sqrtf(ss);
-  const float s1 = nrm * (1.0f / kD);
+  s1 = nrm * (1.0f / kD);
   const float a_t = nrm > 0.f ? kSqrtD / nrm : 0.f;
-  if (hf == 0) ascale[tg] = a_t;
+  if (hf == 0) fs.ascale[tg] = a_t;
   __syncthreads();
 
   // ---- channel-major rotation for the group mean: lane holds tokens
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) av[4 * q + e] = ascale[32 * w + 8 * q + 4 * hf + e];
+      for (int e = 0; e < 4; ++e) av[4 * q + e] = fs.ascale[32 * w + 8 * q + 4 * hf + e];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       v16f c2 = v16f{};
@@ -213,7 +211,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) s = fmaf(av[r], c2[r], s);
       s = half_pair_sum(s);
-      if (hf == 0) csum[w][32 * nb + t] = s;
+      if (hf == 0) fs.csum[w][32 * nb + t] = s;
     }
   }
 #undef HBLK
@@ -221,8 +219,8 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   if (tid < kD) {
     float s = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kNW; ++ww) s += csum[ww][tid];
-    osh[tid] = s * (1.0f / kG);
+    for (int ww = 0; ww < kNW; ++ww) s += fs.csum[ww][tid];
+    fs.osh[tid] = s * (1.0f / kG);
   }
   __syncthreads();
 
@@ -232,7 +230,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 o = *reinterpret_cast<const float4*>(&osh[32 * mb + 8 * q + 4 * hf]);
+      const float4 o = *reinterpret_cast<const float4*>(&fs.osh[32 * mb + 8 * q + 4 * hf]);
       const float ov[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -242,7 +240,43 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       }
     }
   ss2 = half_pair_sum(ss2);
-  const float s2 = sqrtf(ss2 * (1.0f / kD));
+  s2 = sqrtf(ss2 * (1.0f / kD));
+}
+
+__global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
+    const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
+    const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
+    uint16_t* __restrict__ meta, int64_t meta_seq_stride, uint16_t* __restrict__ shift,
+    int64_t shift_seq_stride, int scale_adjust) {
+  // fp16 codebook (the prepared codebook's entries are fp16 values, so this
+  // copy is exact and half the LDS traffic of fp32)
+  __shared__ __attribute__((aligned(16))) uint32_t cbh[kCodes * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t binlut[3 * kFine];   // sentinels around the grid
+  __shared__ FrontSmem fs;
+  // per-lane result row (16 code bytes) that queued sub-vectors update
+  __shared__ __attribute__((aligned(16))) uint32_t res[kNW][kWave][4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int t = lane & 31, hf = lane >> 5;
+  const int64_t seq = blockIdx.x / n_groups;
+  const int64_t grp = blockIdx.x - seq * n_groups;
+  const int tg = 32 * w + t;                          // token within the group
+  const int64_t tok = grp * kG + tg;
+
+  {
+    const uint32_t* cbg = reinterpret_cast<const uint32_t*>(table + kTabCodebookH);
+    for (int i = tid; i < kCodes * 2; i += kG * 2) cbh[i] = cbg[i];
+    const uint32_t* bl = reinterpret_cast<const uint32_t*>(table + kTabBinLut);
+    uint32_t* bd = reinterpret_cast<uint32_t*>(binlut);
+    for (int i = tid; i < 3 * kFine / 4; i += kG * 2)
+      bd[i] = (i >= kFine / 4 && i < 2 * kFine / 4) ? bl[i - kFine / 4] : 0x80808080u;
+  }
+
+  v16f acc[4];
+  float s1, s2;
+  nsn_front(x, x_seq_stride, seq, grp, fs, acc, s1, s2);
+
   // The search runs on z = s2 h directly: distances ||z - s2 c||^2 and bins
   // of z / s2.  A zero z (s2 = 0) is h = 0: scale 1 gives the same answer.
   const float sc = s2 > 0.f ? s2 : 1.0f;
@@ -277,7 +311,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   // so far go to a per-wave queue (in the staging tile, free by now), which
   // the wave then works through one entry per lane, writing an improved code
   // straight into the owner's result row.
-  QEntry* myq = reinterpret_cast<QEntry*>(&xs[w][0]);
+  QEntry* myq = reinterpret_cast<QEntry*>(&fs.xs[w][0]);
   const uint64_t below = (uint64_t(1) << lane) - 1;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -430,19 +464,197 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
                         (static_cast<uint32_t>(f2h(s2 * alpha)) << 16);
     *reinterpret_cast<uint32_t*>(meta + seq * meta_seq_stride + 2 * tok) = mv;
   }
-  if (tid < kD) shift[seq * shift_seq_stride + grp * kD + tid] = f2h(osh[tid]);
+  if (tid < kD) shift[seq * shift_seq_stride + grp * kD + tid] = f2h(fs.osh[tid]);
+}
+
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+}
+
+// fp16 pair (RNE) of (z0 s, z1 s), each rounded once from the exact product.
+// Arithmetic only.
+__device__ __forceinline__ uint32_t split_hi(float z0, float z1, float s) {
+  uint32_t h;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "=v"(h) : "v"(z0), "v"(s));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(h) : "v"(z1), "v"(s));
+  return h;
+}
+// fp16 pair (RNE) of (z0 s - hi0, z1 s - hi1) for hi = split_hi(z0, z1, s),
+// each an fma with one rounding.  Arithmetic only.
+__device__ __forceinline__ uint32_t split_lo(float z0, float z1, float s, uint32_t hi) {
+  uint32_t l;
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,0,1]"
+      : "=v"(l) : "v"(z0), "v"(s), "v"(hi));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "+v"(l) : "v"(z1), "v"(s), "v"(hi));
+  return l;
+}
+// acc + z c for c the low (HI = 0) or high (HI = 1) fp16 half of w (c
+// widened exactly).  Arithmetic only.
+template <int HI>
+__device__ __forceinline__ float fma_acc_f16(float z, uint32_t w, float acc) {
+  float d;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(d) : "v"(z), "v"(w), "v"(acc));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[0,1,0]" : "=v"(d) : "v"(z), "v"(w), "v"(acc));
+  return d;
+}
+
+__global__ __launch_bounds__(kG * 2, 2) void quantize_mfma8_kernel(
+    const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
+    const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
+    uint16_t* __restrict__ meta, int64_t meta_seq_stride, uint16_t* __restrict__ shift,
+    int64_t shift_seq_stride, int scale_adjust) {
+  constexpr int kTiles = kCodes / 32;
+  __shared__ __attribute__((aligned(16))) u32x4 cb8[kCodes];        // fp16 codebook [256][8]
+  // norm operand of tile T for lane l: fp16 (||c||^2 hi, ||c||^2 lo, 1, 0,
+  // 0, ...) of code 32T + l for l < 32, zero for lanes 32..63
+  __shared__ __attribute__((aligned(16))) u32x4 a2s[kTiles][kWave];
+  __shared__ FrontSmem fs;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int t = lane & 31, hf = lane >> 5;
+  const int64_t seq = blockIdx.x / n_groups;
+  const int64_t grp = blockIdx.x - seq * n_groups;
+  const int64_t tok = grp * kG + 32 * (tid >> 6) + t;
+
+  // Codebook operand of tile T: code 32T + t in every lane (K 0..7 in lanes
+  // 0..31 and K 8..15 in lanes 32..63: the same c meets the hi and the lo
+  // part of -2h).
+  const u32x4* cbg = reinterpret_cast<const u32x4*>(table + kTabCodebookH);
+  {
+    const u32x4 c = cbg[tid];                          // 256 threads, one code each
+    cb8[tid] = c;
+    const v8h ch = as_v8h(c);
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) n2 = fmaf(static_cast<float>(ch[e]), static_cast<float>(ch[e]), n2);
+    const _Float16 nh = static_cast<_Float16>(n2);
+    const _Float16 nl = static_cast<_Float16>(n2 - static_cast<float>(nh));   // n2 - nh is exact
+    a2s[tid >> 5][tid & 31] = u32x4{pack_h2(nh, nl), 0x3C00u, 0u, 0u};
+    a2s[tid >> 5][32 + (tid & 31)] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  v16f acc[4];
+  float s1, s2;
+  nsn_front(x, x_seq_stride, seq, grp, fs, acc, s1, s2);   // its barriers publish cb8, a2s
+  // The search runs on g = -2h = z * (-2 / s2) (the factor -2 is exact).  A zero
+  // z (s2 = 0) is h = 0: scale 1 gives the same answer.
+  const float ginv = -2.0f / (s2 > 0.f ? s2 : 1.0f);
+
+  uint32_t cw[4] = {0u, 0u, 0u, 0u};   // code of sub-vector j in byte j % 4 of word j / 4
+  float dot = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // sub-vector j = 4mb + q of the lane's token: this lane holds z of
+      // elements 4hf .. 4hf+3, the other half the rest
+      float zf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t v = __float_as_uint(acc[mb][4 * q + e]);
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        zf[e] = __uint_as_float(r[0]);
+        zf[4 + e] = __uint_as_float(r[1]);
+      }
+      // B1: fp16 hi part of g (lanes 0..31, K 0..7) or lo part g - hi
+      // (lanes 32..63, K 8..15), each rounded once from the exact z * ginv
+      uint32_t b1[4];
+      float gg = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hi = split_hi(zf[2 * i], zf[2 * i + 1], ginv);
+        const uint32_t lo = split_lo(zf[2 * i], zf[2 * i + 1], ginv, hi);
+        b1[i] = hf ? lo : hi;
+        gg = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, hi), __builtin_bit_cast(h2v, hi), gg,
+                                    false);
+      }
+      const v8h B1 = as_v8h(u32x4{b1[0], b1[1], b1[2], b1[3]});
+      // B2: (1, 1, H, 0, ...) in lanes 0..31, H an upper bound of
+      // ||h_j||^2 = ||g||^2 / 4: ||hi||^2 >= (1 - 2^-10) ||g||^2, the 2^-8
+      // increase covers that and the fp16 rounding of H.  Then
+      // D = ||h - c||^2 + (H - ||h_j||^2) >= 0 and its float bits order like
+      // its value.
+      const _Float16 Hh = static_cast<_Float16>(gg * (0.25f * (1.0f + 0x1p-8f)));
+      const v8h B2 = as_v8h(u32x4{hf ? 0u : 0x3C003C00u, hf ? 0u : pack_h2(Hh, 0), 0u, 0u});
+
+      // lane (t, hf) holds D for codes 32T + 8(r/4) + 4hf + r%4, r = 0..15;
+      // the products of tile T + 1 are issued before the minimum of tile T.
+      // (The compiler keeps the loop-invariant operands in registers; forcing
+      // per-tile LDS reads for a third wave per SIMD, or fencing the schedule,
+      // measured slower.)
+      auto tile = [&](int T) {
+        const v16f n = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_v8h(a2s[T][lane]), B2, v16f{},
+                                                              0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_v8h(cb8[32 * T + t]), B1, n, 0, 0, 0);
+      };
+      int best = 0x7fffffff, bt = 0;
+      v16f dcur = tile(0);
+#pragma unroll
+      for (int T = 0; T < kTiles; ++T) {
+        v16f dnext;
+        if (T + 1 < kTiles) dnext = tile(T + 1);
+        int m = 0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          m = min(m, static_cast<int>((__float_as_uint(dcur[r]) & ~15u) | static_cast<uint32_t>(r)));
+        bt = m < best ? T : bt;
+        best = min(best, m);
+        if (T + 1 < kTiles) dcur = dnext;
+      }
+      const uint32_t p = static_cast<uint32_t>(best) & 15u;
+      const uint32_t code = (static_cast<uint32_t>(bt) << 5) | ((p >> 2) << 3) |
+                            (static_cast<uint32_t>(hf) << 2) | (p & 3u);
+      // the two halves hold disjoint code sets of the same token
+      const auto rk = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(best),
+                                                       static_cast<uint32_t>(best), false, false);
+      const auto rc = __builtin_amdgcn_permlane32_swap(code, code, false, false);
+      const int k0 = static_cast<int>(rk[0]), k1 = static_cast<int>(rk[1]);
+      const uint32_t c0 = rc[0], c1 = rc[1];
+      const uint32_t win = (k1 < k0 || (k1 == k0 && c1 < c0)) ? c1 : c0;
+      cw[mb] |= win << (8 * q);
+      // <z_j, c> over all eight elements, for the scale adjustment (both
+      // halves form the same sum in the same order)
+      const u32x4 cv = cb8[win];
+      dot = fma_acc_f16<0>(zf[0], cv.x, dot);
+      dot = fma_acc_f16<1>(zf[1], cv.x, dot);
+      dot = fma_acc_f16<0>(zf[2], cv.y, dot);
+      dot = fma_acc_f16<1>(zf[3], cv.y, dot);
+      dot = fma_acc_f16<0>(zf[4], cv.z, dot);
+      dot = fma_acc_f16<1>(zf[5], cv.z, dot);
+      dot = fma_acc_f16<0>(zf[6], cv.w, dot);
+      dot = fma_acc_f16<1>(zf[7], cv.w, dot);
+    }
+  }
+
+  // <h, h_hat> = <z, h_hat> / s2 and ||h||^2 = d exactly (Normalize #2)
+  const float alpha = (scale_adjust && dot > 0.f) ? (kD * s2) / dot : 1.0f;
+  if (hf == 0) {
+    *reinterpret_cast<u32x4*>(codes + seq * codes_seq_stride + tok * 16) =
+        u32x4{cw[0], cw[1], cw[2], cw[3]};
+    const uint32_t mv = static_cast<uint32_t>(f2h(s1)) |
+                        (static_cast<uint32_t>(f2h(s2 * alpha)) << 16);
+    *reinterpret_cast<uint32_t*>(meta + seq * meta_seq_stride + 2 * tok) = mv;
+  }
+  if (tid < kD) shift[seq * shift_seq_stride + grp * kD + tid] = f2h(fs.osh[tid]);
 }
 
 }  // namespace
 
 bool quantize_mfma_supported(int in_f32, int sub_dim, int group_size) {
-  return !in_f32 && sub_dim == 4 && group_size == kG;
+  return !in_f32 && (sub_dim == 4 || sub_dim == 8) && group_size == kG;
 }
 
 hipError_t launch_quantize_mfma(const QuantArgs& a, hipStream_t s) {
   const int64_t n_groups = a.n_tok / kG;
   const int64_t blocks = a.n_seq * n_groups;
-  hipLaunchKernelGGL(quantize_mfma_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kG * 2), 0, s,
+  hipLaunchKernelGGL(a.sub_dim == 8 ? quantize_mfma8_kernel : quantize_mfma_kernel,
+                     dim3(static_cast<unsigned>(blocks)), dim3(kG * 2), 0, s,
                      static_cast<const __half*>(a.x), n_groups, a.x_seq_stride,
                      static_cast<const uint8_t*>(a.table), a.codes, a.codes_seq_stride, a.meta,
                      a.meta_seq_stride, a.shift, a.shift_seq_stride, a.scale_adjust);

@@ -44,7 +44,7 @@ def test_quantize_parity_workloads(name):
     _say(f"  {name}: {ties} accepted near-ties of {total} codes")
 
 
-@pytest.mark.parametrize("m,G", [(4, 128), (8, 256)])
+@pytest.mark.parametrize("m,G", [(4, 128), (8, 128), (8, 256)])
 def test_quantize_ragged_strided_into_cache(m, G):
     """Three sequences, three groups each, written at a group offset inside
     larger caches (sequence strides bigger than the data)."""
@@ -72,9 +72,11 @@ def test_quantize_scale_adjust_off():
     _check_all(K, C, 128, codes, meta, shift, scale_adjust=False)
 
 
-def test_quantize_degenerate_tokens():
+@pytest.mark.parametrize("m", [4, 8])
+def test_quantize_degenerate_tokens(m):
     """Zero token, all-zero group, constant group, huge and tiny magnitudes."""
     G = 128
+    _say(f"quantize degenerate tokens m={m}")
     rng = np.random.default_rng(7)
     x = rng.standard_normal((1, 4 * G, 128)).astype(np.float16)
     x[0, 5] = 0                                    # zero token
@@ -83,7 +85,7 @@ def test_quantize_degenerate_tokens():
     x[0, 3 * G + 1] *= 1000                        # large
     x[0, 3 * G + 2] = (x[0, 3 * G + 2].astype(np.float32) * 1e-3).astype(np.float16)
     x[0, 3 * G + 3] = 60000.0 * np.sign(x[0, 3 * G + 3] + 0.1).astype(np.float16)
-    codes, meta, shift, _, (p, table, C) = quantize_gpu(x, 4, G)
+    codes, meta, shift, _, (p, table, C) = quantize_gpu(x, m, G)
     assert np.isfinite(meta.astype(np.float32)).all() and np.isfinite(shift.astype(np.float32)).all()
     assert meta[0, 5, 0] == 0 and np.all(meta[0, G:2 * G] == 0) and np.all(shift[0, 1] == 0)
     # In the all-zero group h = 0, and in the constant group z is rounding
@@ -96,10 +98,11 @@ def test_quantize_degenerate_tokens():
     assert rel_l2(xr, x[0, 2 * G:3 * G]) < 2e-3
 
 
-def test_quantize_is_deterministic():
+@pytest.mark.parametrize("m", [4, 8])
+def test_quantize_is_deterministic(m):
     K, V = synth.kv_numpy(4, 1024, 5.0, seed=8, dtype=np.float16)
-    a = quantize_gpu(K, 4, 128)
-    b = quantize_gpu(K, 4, 128, p_table=a[4])
+    a = quantize_gpu(K, m, 128)
+    b = quantize_gpu(K, m, 128, p_table=a[4])
     for i in range(3):
         assert np.array_equal(a[i], b[i])
 
