@@ -41,4 +41,10 @@ from .nsn import (  # noqa: F401
     sq_dist_exact,
 )
 from .codebook import kmeans_codebook, round_to_fp16  # noqa: F401
-from .attention import decode_attention, decode_attention_rotated, attend  # noqa: F401
+from .attention import (  # noqa: F401
+    apply_rope,
+    attend,
+    decode_attention,
+    decode_attention_rope,
+    decode_attention_rotated,
+)

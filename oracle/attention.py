@@ -26,13 +26,27 @@ Pins (tests/test_oracle_attention.py): agreement with a plain per-head loop
 using scipy.special.softmax; the rotated-domain identity; q = 0 gives the
 mean of the values; Nq = 0 gives plain attention over the residual; a single
 key returns its value.
+
+``decode_attention_rope`` is the same attention with the keys stored before
+rotary position embedding, the order the pages give for keys (Methodology
+§4: NSN is applied to keys before RoPE).  The pages fix neither the RoPE
+variant nor its base nor the positions; readings: the rotate-half form
+(channel pairs (i, i + d/2), frequency theta_i = base^(-2i/d)), a caller-given
+base, cache token t at position t, residual token r at position n_quant + r,
+and the query at a caller-given position; RoPE is applied to the query and
+to every key (dequantized or residual), values are unchanged.  Pins: the
+closed forms of the pair rotation (sin and cos of the position difference
+times the pair's frequency), norm preservation, composition of rotations,
+invariance of the output under a common position shift, and reduction to
+``decode_attention`` when every position is zero.
 """
 
 import numpy as np
 
 from .nsn import dequantize, rotate
 
-__all__ = ["attend", "decode_attention", "decode_attention_rotated"]
+__all__ = ["attend", "decode_attention", "decode_attention_rotated", "apply_rope",
+           "decode_attention_rope"]
 
 
 def attend(q, keys, values, scale):
@@ -116,4 +130,50 @@ def decode_attention_rotated(q, k_cache, v_cache, k_resid, v_resid, C, G,
                 acc_rot += wg @ vs[:n_quant // G].astype(np.float64)
             vr = np.asarray(v_resid[b, kvh, :n_resid], np.float64)
             out[b, h] = rotate(acc_rot) + p[n_quant:] @ vr
+    return out
+
+
+def apply_rope(x, pos, base):
+    """Rotate-half rotary embedding in float64: for i < d/2 the channel pair
+    (x_i, x_{i+d/2}) is rotated by the angle pos * base^(-2i/d).
+    x (..., d); pos broadcasts against x's leading dimensions."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    theta = float(base) ** (-2.0 * np.arange(half) / d)
+    ang = np.asarray(pos, np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def attend_rope(q, keys, values, scale, q_pos, key_pos, base):
+    """``attend`` with RoPE applied to the query (at q_pos) and to every key
+    (at key_pos[t])."""
+    return attend(apply_rope(q, q_pos, base), apply_rope(keys, key_pos, base), values, scale)
+
+
+def decode_attention_rope(q, k_cache, v_cache, k_resid, v_resid, C, G, n_quant,
+                          n_resid, scale, q_pos, base, heads=None):
+    """``decode_attention`` over keys stored before RoPE: key t of a (b, kv
+    head) row (quantized tokens first, then the residual) sits at position t,
+    the query at q_pos.  Same arguments plus q_pos and the RoPE base."""
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_cache[0].shape[1]
+    grp = Hq // Hkv
+    out = np.full((B, Hq, d), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    cached = {}
+    for b, h in todo:
+        kvh = h // grp
+        if (b, kvh) not in cached:
+            keys = np.concatenate([_kv_rows(k_cache, b, kvh, n_quant, C, G),
+                                   np.asarray(k_resid[b, kvh, :n_resid], np.float64)])
+            vals = np.concatenate([_kv_rows(v_cache, b, kvh, n_quant, C, G),
+                                   np.asarray(v_resid[b, kvh, :n_resid], np.float64)])
+            cached = {(b, kvh): (keys, vals)}
+        keys, vals = cached[(b, kvh)]
+        out[b, h] = attend_rope(q[b, h], keys, vals, scale, q_pos,
+                                np.arange(keys.shape[0]), base)
     return out
