@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 D = 128
 COPY_CAL_BYTES = 1 << 30
+ROPE_BASE = 10000.0          # rotary base of the rotary-key side measurement
 QUANT_SRC = os.path.join(ROOT, "kv_cache_calibration_amd", "csrc", "quantize_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_mfma_prefill_hbm_bytes.txt")
 
@@ -237,6 +238,21 @@ def main():
     torch.cuda.synchronize()
     ms_attn1 = float(np.mean([a.elapsed_time(b) for a, b in ev1]))
 
+    # side measurement, outside the step: the 2-bit decode attention with the
+    # keys stored before rotary embedding (query at the last residual position)
+    evr = []
+    for i in range(max(args.steps, 3) + 1):
+        kc, vc, kr, vr, q = caches[i % 3]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nsnq.nsn_decode_attention_rope(p, q, kc, vc, kr, vr, table, work, out, Nq, R, scale,
+                                       Nq + R - 1, ROPE_BASE)
+        b.record(stream)
+        if i > 0:
+            evr.append((a, b))
+    torch.cuda.synchronize()
+    ms_attn_rope = float(np.mean([a.elapsed_time(b) for a, b in evr]))
+
     # side measurement, outside the step: the same prefill quantize with
     # 1-bit codes (its metadata and shifts overwrite the step's outputs)
     codes1 = torch.empty((n_seq, cap, D // m1), dtype=torch.uint8, device=dev)
@@ -267,6 +283,8 @@ def main():
         "attention_1bit_gbps": attn_bytes(B3, Hq, Hkv, Nq, R, m1, G) / (ms_attn1 * 1e-3) / 1e9,
         "attention_1bit_ms": ms_attn1,
         "attention_query_tokens_per_s": B3 / (ms["attention"] * 1e-3),
+        "attention_rope_gbps": ab / (ms_attn_rope * 1e-3) / 1e9,
+        "attention_rope_ms": ms_attn_rope,
         "quantize_1bit_gbps": quant_bytes(n_seq, T, m1, G) / (ms_q1 * 1e-3) / 1e9,
         "quantize_1bit_ms": ms_q1,
         "flush_gbps": fb / (ms["flush"] * 1e-3) / 1e9,
@@ -276,6 +294,7 @@ def main():
     rates["attention_frac_hbm"] = rates["attention_gbps"] / HBM_PEAK_GBPS
     rates["attention_1bit_frac_hbm"] = rates["attention_1bit_gbps"] / HBM_PEAK_GBPS
     rates["quantize_1bit_frac_hbm"] = rates["quantize_1bit_gbps"] / HBM_PEAK_GBPS
+    rates["attention_rope_frac_hbm"] = rates["attention_rope_gbps"] / HBM_PEAK_GBPS
     log("kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ms.items()))
     log("rates: " + ", ".join(f"{k} {v:.4g}" for k, v in rates.items()))
 

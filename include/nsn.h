@@ -220,6 +220,39 @@ nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s,
                                 void* workspace, size_t workspace_bytes,
                                 float* out, void* stream);
 
+/*
+ * nsn_decode_attention_rope -- nsn_decode_attention for keys stored before
+ * rotary position embedding.
+ * [NSNQuant summary §4: for keys, NSN is applied before RoPE; the score
+ *  still takes the NSN byproducts.]
+ *
+ * The pages fix neither the RoPE form, its base nor the positions.  This
+ * call uses the rotate-half form: for i < 64 the channel pair (i, i + 64)
+ * of a vector at position pos turns by the angle pos * base^(-i/64)
+ * ((x, y) -> (x cos - y sin, y cos + x sin)).  Quantized key t of a (b, kv
+ * head) row sits at position t, residual key r at n_quant_tok + r, the
+ * query at rope->q_pos; the query and every key are turned before the dot
+ * product (the query arrives un-rotated, like the keys).  Values are
+ * unchanged.  Everything else -- arguments, layouts, workspace size (the
+ * same nsn_decode_attention_workspace_size()), ordering and errors -- is as
+ * for nsn_decode_attention.
+ *
+ * rope     host; base finite and > 1, 0 <= q_pos <= 2^40, else
+ *          NSN_ERR_INVALID_ARG.
+ */
+typedef struct {
+  int64_t q_pos;   /* position of the query token */
+  float base;      /* rotary base, e.g. 10000 */
+} nsn_rope;
+nsn_status nsn_decode_attention_rope(const nsn_params* p, const nsn_attn_shape* s,
+                                     const nsn_rope* rope, const uint16_t* q,
+                                     const uint8_t* k_codes, const uint16_t* k_meta,
+                                     const uint16_t* k_shift, const uint8_t* v_codes,
+                                     const uint16_t* v_meta, const uint16_t* v_shift,
+                                     const uint16_t* k_resid, const uint16_t* v_resid,
+                                     const void* table, void* workspace, size_t workspace_bytes,
+                                     float* out, void* stream);
+
 /* Static description of a status code. */
 const char* nsn_status_string(nsn_status s);
 /* Detail of the last error returned on the calling thread ("" if none). */

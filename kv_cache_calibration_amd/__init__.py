@@ -30,6 +30,7 @@ __all__ = [
     "nsn_dequantize",
     "nsn_residual_append",
     "nsn_decode_attention",
+    "nsn_decode_attention_rope",
     "nsn_decode_attention_workspace_size",
     "lib_path",
 ]
@@ -190,11 +191,29 @@ def nsn_decode_attention_workspace_size(params, batch, n_q_heads, n_kv_heads, n_
                                                                ctypes.byref(s)))
 
 
+def nsn_decode_attention_rope(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace,
+                              out, n_quant_tok, n_resid_tok, softmax_scale, q_pos, rope_base,
+                              stream=None):
+    """nsn_decode_attention for keys stored before rotary embedding: the query
+    (at q_pos) and every key (quantized key t at position t, residual key r at
+    n_quant_tok + r) are turned by the rotate-half rotary embedding with the
+    given base.  Same tensors as nsn_decode_attention."""
+    _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
+                      n_quant_tok, n_resid_tok, softmax_scale, stream,
+                      _lib.nsn_rope(int(q_pos), float(rope_base)))
+
+
 def nsn_decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
                          n_quant_tok, n_resid_tok, softmax_scale, stream=None):
     """q fp16 (B, Hq, 128); k_cache/v_cache = (codes (B, Hkv, cap, 128/m) uint8,
     meta (B, Hkv, cap, 2) fp16, shift (B, Hkv, cap/G, 128) fp16), all contiguous;
     k_resid/v_resid fp16 (B, Hkv, Rcap, 128) contiguous; out fp32 (B, Hq, 128)."""
+    _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
+                      n_quant_tok, n_resid_tok, softmax_scale, stream, None)
+
+
+def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
+                      n_quant_tok, n_resid_tok, softmax_scale, stream, rope):
     kc, km, ks = k_cache
     vc, vm, vs = v_cache
     _dev(q, kc, km, ks, vc, vm, vs, k_resid, v_resid, table, workspace, out)
@@ -205,7 +224,11 @@ def nsn_decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, w
     Hkv, cap = kc.shape[1], kc.shape[2]
     s = _shape(B, Hq, Hkv, n_quant_tok, n_resid_tok, cap, k_resid.shape[2], softmax_scale)
     lib = _lib.load()
-    _lib.check(lib.nsn_decode_attention(
-        ctypes.byref(params.c), ctypes.byref(s), _ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc),
-        _ptr(vm), _ptr(vs), _ptr(k_resid), _ptr(v_resid), _ptr(table), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+    bufs = (_ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc), _ptr(vm), _ptr(vs), _ptr(k_resid),
+            _ptr(v_resid), _ptr(table), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
+    if rope is None:
+        _lib.check(lib.nsn_decode_attention(ctypes.byref(params.c), ctypes.byref(s), *bufs))
+    else:
+        _lib.check(lib.nsn_decode_attention_rope(ctypes.byref(params.c), ctypes.byref(s),
+                                                 ctypes.byref(rope), *bufs))

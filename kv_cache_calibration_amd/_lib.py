@@ -43,6 +43,13 @@ class nsn_attn_shape(ctypes.Structure):
     ]
 
 
+class nsn_rope(ctypes.Structure):
+    _fields_ = [
+        ("q_pos", ctypes.c_int64),
+        ("base", ctypes.c_float),
+    ]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -65,6 +72,9 @@ SIGNATURES = {
                                                   ctypes.POINTER(nsn_attn_shape)]),
     "nsn_decode_attention": (_ST, [ctypes.POINTER(nsn_params), ctypes.POINTER(nsn_attn_shape),
                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "nsn_decode_attention_rope": (_ST, [ctypes.POINTER(nsn_params), ctypes.POINTER(nsn_attn_shape),
+                                        ctypes.POINTER(nsn_rope), _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _SZ, _P, _P]),
     "nsn_status_string": (ctypes.c_char_p, [_ST]),
     "nsn_last_error": (ctypes.c_char_p, []),
     "nsn_version": (ctypes.c_char_p, []),

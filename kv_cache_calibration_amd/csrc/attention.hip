@@ -77,6 +77,8 @@ struct SplitParams {
   int Hq, Hkv, grp, hblocks, n_quant, n_split, chunk, n_resid;
   int64_t cap, rcap;
   float scale;
+  int64_t q_pos;     // query position (keys stored before rotary embedding)
+  float rope_base;   // rotary base, theta_i = base^(-i/64)
 };
 
 template <int M>
@@ -102,6 +104,20 @@ template <int M>
 union AttnSmem {
   SplitSmem<M> s;
   ResidSmem r;
+};
+// Keys stored before rotary embedding: every tile of 64 keys (positions
+// P .. P + 63) is scored as <R(q_pos - P) q, R(t) k_t> = <R(q_pos) q,
+// R(P + t) k_t>, so the per-key rotation R(t) depends only on the key's
+// offset t in the tile (a table built once per workgroup) and the query is
+// turned once per tile.
+struct RopeSmem {
+  float2 tab[kD / 2][kTile];     // (cos, sin) of t * theta_i, [pair i][offset t]
+  float q[kHB][kD];              // the block's queries, original domain
+  float qp[kWaves][kHB][kD];     // per wave: the queries turned by q_pos - P
+  float og[kWaves][kD];          // per wave: the tile's group shift, original domain
+};
+struct NoRopeSmem {
+  int unused;
 };
 
 // ds_read_b64_tr_b16: inside each group of 16 lanes, lane 4a + b receives
@@ -223,13 +239,111 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A operands of the Sylvester matrix H128 = H8 (x) H16 for
+// v_mfma_f32_32x32x16_f16: block (a, kb) (rows 32a.., K slice 16kb..) is
+// +-(one 16-column pattern), the sign (-1)^popcount(2a & kb), times the
+// bit-4 row sign for odd kb.  +-1 are exact in fp16.
+struct HOps {
+  u32x4 P0, P1, N0, N1;
+};
+__device__ __forceinline__ HOps hadamard_ops(int lane) {
+  const int r16 = lane & 15, r4 = (lane >> 4) & 1, hf = lane >> 5;
+  uint32_t wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c0 = 8 * hf + 2 * i, c1 = c0 + 1;
+    const uint32_t lo = (__popc(r16 & c0) & 1) ? 0xBC00u : 0x3C00u;
+    const uint32_t hi = (__popc(r16 & c1) & 1) ? 0xBC00u : 0x3C00u;
+    wv[i] = lo | (hi << 16);
+  }
+  HOps o;
+  o.P0 = u32x4{wv[0], wv[1], wv[2], wv[3]};
+  const uint32_t f = r4 ? 0x80008000u : 0u;
+  o.P1 = u32x4{wv[0] ^ f, wv[1] ^ f, wv[2] ^ f, wv[3] ^ f};
+  o.N0 = o.P0 ^ 0x80008000u;
+  o.N1 = o.P1 ^ 0x80008000u;
+  return o;
+}
+typedef float v16f __attribute__((ext_vector_type(16)));
+// block (a, kb); a and kb are constants once the caller's loops unroll
+__device__ __forceinline__ v8h hblk(const HOps& o, int a, int kb) {
+  const bool neg = (__popc((2 * a) & kb) & 1) != 0;
+  return __builtin_bit_cast(v8h, (kb & 1) ? (neg ? o.N1 : o.P1) : (neg ? o.N0 : o.P0));
+}
+
+// Rotary angle: theta_i = base^(-i/64) for channel pair (i, i + 64).
+__device__ __forceinline__ double rope_theta(float base, int i) {
+  return pow(static_cast<double>(base), -static_cast<double>(i) / 64.0);
+}
+// (cos a, sin a), the angle reduced to [-pi, pi] in double first.
+__device__ __forceinline__ float2 rope_cs(double a) {
+  const double two_pi = 6.283185307179586476925;
+  const double r = a - two_pi * rint(a * (1.0 / two_pi));
+  float sn, cs;
+  sincosf(static_cast<float>(r), &sn, &cs);
+  return make_float2(cs, sn);
+}
+// The wave's queries turned by the angle delta * theta (lane = pair i):
+// pair (x, y) -> (x cos - y sin, y cos + x sin).  The caller syncs the wave.
+__device__ __forceinline__ void rope_query(const RopeSmem& rs, float (&qp)[kHB][kD], int lane,
+                                           double theta, int64_t delta) {
+  const float2 cs = rope_cs(static_cast<double>(delta) * theta);
+#pragma unroll
+  for (int h = 0; h < kHB; ++h) {
+    const float x = rs.q[h][lane], y = rs.q[h][lane + kD / 2];
+    qp[h][lane] = x * cs.x - y * cs.y;
+    qp[h][lane + kD / 2] = y * cs.x + x * cs.y;
+  }
+}
+// Scores (base-2 units) of the lane's key k (original domain, before the
+// rotary embedding; k[c] = a hc[c] + b og[c]) at offset `lane` of its tile
+// against the turned queries qp.
+__device__ __forceinline__ void rope_dot(float (&s)[kHB], const float (&hc)[kD], float a, float bo,
+                                         const float* og, const RopeSmem& rs,
+                                         const float (&qp)[kHB][kD], int lane, float qscale) {
+  float acc[kHB] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i0 = 0; i0 < kD / 2; i0 += 4) {
+    float ox[4] = {0.f, 0.f, 0.f, 0.f}, oy[4] = {0.f, 0.f, 0.f, 0.f};
+    if (og) {
+      const float4 u = *reinterpret_cast<const float4*>(og + i0);
+      const float4 v = *reinterpret_cast<const float4*>(og + kD / 2 + i0);
+      ox[0] = u.x; ox[1] = u.y; ox[2] = u.z; ox[3] = u.w;
+      oy[0] = v.x; oy[1] = v.y; oy[2] = v.z; oy[3] = v.w;
+    }
+    float qx[kHB][4], qy[kHB][4];
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      const float4 u = *reinterpret_cast<const float4*>(&qp[h][i0]);
+      const float4 v = *reinterpret_cast<const float4*>(&qp[h][kD / 2 + i0]);
+      qx[h][0] = u.x; qx[h][1] = u.y; qx[h][2] = u.z; qx[h][3] = u.w;
+      qy[h][0] = v.x; qy[h][1] = v.y; qy[h][2] = v.z; qy[h][3] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e;
+      const float2 cs = rs.tab[i][lane];
+      const float x = fmaf(a, hc[i], bo * ox[e]);
+      const float y = fmaf(a, hc[i + kD / 2], bo * oy[e]);
+      const float kx = x * cs.x - y * cs.y;
+      const float ky = y * cs.x + x * cs.y;
+#pragma unroll
+      for (int h = 0; h < kHB; ++h) acc[h] = fmaf(qy[h][e], ky, fmaf(qx[h][e], kx, acc[h]));
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kHB; ++h) s[h] = acc[h] * qscale;
+}
+
 // The fp16 residual window of one (batch, kv head, head block), in the
 // original domain, written as partial n_split.  Every load is issued first;
 // scores are exact MFMA products of the fp16 q and k (fp32 sums) into LDS;
 // after one barrier every wave takes the per-head max and sum itself; values
 // run one thread per (channel pair, token residue mod 4) with weights formed
 // on the fly, and the four residue classes are summed through LDS.
-__device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh, int hb) {
+template <bool ROPE>
+__device__ void resid_block(const SplitParams& p, ResidSmem& sm, RopeSmem* rs, double theta, int b,
+                            int kvh, int hb) {
   constexpr int kVPre = 32;              // value words held in registers per thread
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -251,6 +365,31 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
     const int t = wave + kWaves * i;
     vpre[i] = t < nr ? vrow[static_cast<int64_t>(t) * (kD / 2) + lane] : 0u;
   }
+  if constexpr (ROPE) {
+    // keys before rotary embedding, positions n_quant + t: tiles of 64, lane
+    // = token, wave w takes tiles w, w + 4, ...
+    for (int rt = wave; rt * kTile < nr; rt += kWaves) {
+      const int t = rt * kTile + lane;
+      rope_query(*rs, rs->qp[wave], lane, theta, p.q_pos - (static_cast<int64_t>(p.n_quant) + rt * kTile));
+      float hc[kD];
+#pragma unroll
+      for (int i = 0; i < kD / 8; ++i) {
+        const u32x4 w = t < nr ? *reinterpret_cast<const u32x4*>(krow + static_cast<int64_t>(t) * kD + 8 * i)
+                               : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hc[8 * i + 2 * k] = h2f(ww[k] & 0xffffu);
+          hc[8 * i + 2 * k + 1] = h2f(ww[k] >> 16);
+        }
+      }
+      wave_lds_sync();
+      float sc[kHB];
+      rope_dot(sc, hc, 1.0f, 0.f, nullptr, *rs, rs->qp[wave], lane, qscale);
+      if (t < nr) sm.sres[t] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+      wave_lds_sync();
+    }
+  } else {
   // A operand per step s: row c16 = head c16 (< nh), K index 8R + v =
   // channel 32 s + 8R + v
   u32x4 qa[4];
@@ -278,6 +417,7 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
       if (R == 0 && t < nr)
         sm.sres[t] = make_float4(d[0] * qscale, d[1] * qscale, d[2] * qscale, d[3] * qscale);
     }
+  }
   }
   __syncthreads();
   // ---- per-head max and sum, every wave over all tokens
@@ -349,11 +489,12 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, int b, int kvh,
   }
 }
 
-template <int M, int G>
-__global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(SplitParams p) {
+template <int M, int G, bool ROPE>
+__global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_kernel(SplitParams p) {
   constexpr int CB = kD / M;            // code bytes per token
   constexpr int TPG = G / kTile;        // tiles per group
   __shared__ AttnSmem<M> smem;
+  __shared__ std::conditional_t<ROPE, RopeSmem, NoRopeSmem> rsm;
   SplitSmem<M>& sm = smem.s;
 
   const int tid = threadIdx.x;
@@ -364,15 +505,30 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
   const int kvh = blockIdx.y / p.hblocks;
   const int hb = blockIdx.y - kvh * p.hblocks;
   const int b = blockIdx.z;
+  const int h0 = kvh * p.grp + hb * kHB;
+  const int nh = min(kHB, p.grp - hb * kHB);
+  double theta = 0.0;   // rotary frequency of pair `lane`
+  RopeSmem* rsp = nullptr;
+  if constexpr (ROPE) {
+    rsp = &rsm;
+    theta = rope_theta(p.rope_base, lane);
+    for (int idx = tid; idx < (kD / 2) * kTile; idx += kThreads) {
+      const int i = idx / kTile, t = idx % kTile;
+      rsm.tab[i][t] = rope_cs(static_cast<double>(t) * rope_theta(p.rope_base, i));
+    }
+    for (int idx = tid; idx < kHB * kD; idx += kThreads) {
+      const int h = idx / kD, c = idx % kD;
+      rsm.q[h][c] = h < nh ? h2f(p.q[(static_cast<int64_t>(b) * p.Hq + h0 + h) * kD + c]) : 0.f;
+    }
+    __syncthreads();
+  }
   if (split == 0) {
     // the residual window first: its load latency overlaps the other
     // workgroups' work instead of ending the kernel
-    resid_block(p, smem.r, b, kvh, hb);
+    resid_block<ROPE>(p, smem.r, rsp, theta, b, kvh, hb);
     if (p.n_split == 0) return;
     __syncthreads();   // the LDS is reused
   }
-  const int h0 = kvh * p.grp + hb * kHB;
-  const int nh = min(kHB, p.grp - hb * kHB);
   const int c0 = split * p.chunk;
   const int c1 = min(p.n_quant, c0 + p.chunk);
   const int ntiles = (c1 - c0) / kTile;   // chunks hold whole groups, groups whole tiles
@@ -409,7 +565,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
   }
   __syncthreads();
   // <q'_h, o'_g> for every group of the chunk, one thread per (g, h)
-  for (int idx = tid; idx < ng * kHB; idx += kThreads) {
+  for (int idx = tid; idx < (ROPE ? 0 : ng * kHB); idx += kThreads) {
     const int g = idx / kHB, h = idx % kHB;
     const uint4* o = reinterpret_cast<const uint4*>(ksg + static_cast<int64_t>(g) * kD);
     float s = 0.f;
@@ -429,7 +585,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
   // fp16(q'_h - fp16(q'_h)), the pair carries ~22 bits; 8..15: 0), K index
   // 8R + v = channel 32R + 8s + v
   u32x4 qa[4];
-  {
+  if constexpr (!ROPE) {
     const int hq = c16 & 3;
     const bool is_hi = c16 < 4, is_lo = c16 >= 4 && c16 < 8;
 #pragma unroll
@@ -477,14 +633,131 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
   const uint32_t wtr = lds_addr(&sm.wrow[wave][8 * R + k4][4 * a4]);
 
   TileData<M> d;
+  HOps ho{};
+  if constexpr (ROPE) ho = hadamard_ops(lane);
   for (int tau = wave; tau < ntiles; tau += kWaves) {
     const int tn = tau + kWaves;
     const bool more = tn < ntiles;
     if (tau == wave) {
-      load_keys<M>(d, kcrow + tau * kTile * CB, koff);
+      if constexpr (!ROPE) load_keys<M>(d, kcrow + tau * kTile * CB, koff);
       load_meta<M>(d, kmrow + tau * kTile, vmrow + tau * kTile, lane);
       load_values<M>(d, vcrow + tau * kTile * CB, voff);
     }
+    float s[kHB];
+    float s1v, s2v;
+    if constexpr (ROPE) {
+      // the tile's group shift in the original domain, (H / sqrt(d)) o'_g,
+      // lane holding channels 2 lane, 2 lane + 1; the queries turned to the
+      // tile's first position
+      {
+        const uint32_t ww = reinterpret_cast<const uint32_t*>(ksg + static_cast<int64_t>(tau / TPG) * kD)[lane];
+        float x0 = h2f(ww & 0xffffu), x1 = h2f(ww >> 16);
+        const float u0 = x0 + x1, u1 = x0 - x1;
+        x0 = u0;
+        x1 = u1;
+#pragma unroll
+        for (int e = 1; e < kWave; e <<= 1) {
+          const float y0 = __shfl_xor(x0, e, kWave), y1 = __shfl_xor(x1, e, kWave);
+          const bool up = (lane & e) != 0;
+          x0 = up ? y0 - x0 : x0 + y0;
+          x1 = up ? y1 - x1 : x1 + y1;
+        }
+        *reinterpret_cast<float2*>(&rsm.og[wave][2 * lane]) = make_float2(x0 * kInvSqrtD, x1 * kInvSqrtD);
+      }
+      rope_query(rsm, rsm.qp[wave], lane, theta, p.q_pos - (static_cast<int64_t>(c0) + tau * kTile));
+      wave_lds_sync();
+      // Two halves of 32 keys.  The MFMA token-major pass gives lane
+      // (t32, hf) the channels {32mb + 8(r/4) + 4hf + r%4} of key 32ht + t32:
+      // both members of every rotary pair (c, c + 64) sit in one lane.
+      const int t32 = lane & 31, hf = lane >> 5;
+      // (scheduling fences around the two halves and the two row-block pairs
+      // keep their registers from overlapping; without them the kernel spills)
+      __builtin_amdgcn_sched_barrier(0);
+      float sh[kHB];   // key 32 hf + t32 ends up in this lane: half ht == hf keeps its sums
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const int tok = 32 * ht + t32;   // key of the tile
+        const uint8_t* kt = kcrow + (tau * kTile + tok) * CB;
+        u32x4 xv[8];   // channels 16kb + 8hf .. + 7 of the key, codewords (fp16, exact)
+        if constexpr (M == 4) {
+          const u32x4 w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt));
+          const u32x4 w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt) + 1);
+          const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            // sub-vectors 4kb + 2hf and + 1: bytes 2hf, 2hf + 1 of word kb
+            const uint32_t wq = ww[kb] >> (16 * hf);
+            const uint32_t c0i = wq & 0xffu, c1i = (wq >> 8) & 0xffu;
+            const u32x2 a0 = *reinterpret_cast<const u32x2*>(&sm.cbh[2 * c0i]);
+            const u32x2 a1 = *reinterpret_cast<const u32x2*>(&sm.cbh[2 * c1i]);
+            xv[kb] = u32x4{a0.x, a0.y, a1.x, a1.y};
+          }
+        } else {
+          const u32x4 w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt));
+          const uint32_t ww[4] = {w0.x, w0.y, w0.z, w0.w};
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            // sub-vector 2kb + hf: byte 2(kb % 2) + hf of word kb / 2
+            const uint32_t ci = (ww[kb >> 1] >> (8 * (2 * (kb & 1) + hf))) & 0xffu;
+            xv[kb] = *reinterpret_cast<const u32x4*>(&sm.cbh[4 * ci]);
+          }
+        }
+        // k = s1 (s2' H c / sqrt(d) + og), turned by the key's offset, dotted
+        // with the turned queries over this lane's 64 channels; row blocks
+        // (pm, pm + 2) hold the pairs (c, c + 64) of channels 32pm ..
+        const uint32_t kmt = __shfl(d.km, tok, kWave);
+        const float s1k = h2f(kmt & 0xffffu), s2k = h2f(kmt >> 16);
+        const float a = s1k * s2k * kInvSqrtD;
+        float part[kHB] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pm = 0; pm < 2; ++pm) {
+          v16f hx = v16f{}, hy = v16f{};
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            hx = __builtin_amdgcn_mfma_f32_32x32x16_f16(hblk(ho, pm, kb), __builtin_bit_cast(v8h, xv[kb]), hx, 0, 0, 0);
+            hy = __builtin_amdgcn_mfma_f32_32x32x16_f16(hblk(ho, pm + 2, kb), __builtin_bit_cast(v8h, xv[kb]), hy, 0, 0, 0);
+          }
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int cb0 = 32 * pm + 8 * g4 + 4 * hf;   // channels cb0 .. cb0 + 3 and + 64
+            const float4 ox = *reinterpret_cast<const float4*>(&rsm.og[wave][cb0]);
+            const float4 oy = *reinterpret_cast<const float4*>(&rsm.og[wave][cb0 + kD / 2]);
+            const float oxv[4] = {ox.x, ox.y, ox.z, ox.w}, oyv[4] = {oy.x, oy.y, oy.z, oy.w};
+            float qx[kHB][4], qy[kHB][4];
+#pragma unroll
+            for (int h = 0; h < kHB; ++h) {
+              const float4 u = *reinterpret_cast<const float4*>(&rsm.qp[wave][h][cb0]);
+              const float4 v = *reinterpret_cast<const float4*>(&rsm.qp[wave][h][cb0 + kD / 2]);
+              qx[h][0] = u.x; qx[h][1] = u.y; qx[h][2] = u.z; qx[h][3] = u.w;
+              qy[h][0] = v.x; qy[h][1] = v.y; qy[h][2] = v.z; qy[h][3] = v.w;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g4 + e;
+              const float2 cs = rsm.tab[cb0 + e][tok];
+              const float x = fmaf(a, hx[r], s1k * oxv[e]);
+              const float y = fmaf(a, hy[r], s1k * oyv[e]);
+              const float kx = x * cs.x - y * cs.y;
+              const float ky = y * cs.x + x * cs.y;
+#pragma unroll
+              for (int h = 0; h < kHB; ++h) part[h] = fmaf(qy[h][e], ky, fmaf(qx[h][e], kx, part[h]));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int h = 0; h < kHB; ++h) {
+          const float v = half_pair_sum(part[h]);
+          sh[h] = ht == hf ? v : sh[h];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int h = 0; h < kHB; ++h) s[h] = sh[h] * qscale;
+      s1v = h2f(d.vm & 0xffffu);
+      s2v = h2f(d.vm >> 16);
+      if (more) load_meta<M>(d, kmrow + tn * kTile, vmrow + tn * kTile, lane);
+    } else {
     // -- scores
     v4f sacc[4];
 #pragma unroll
@@ -511,12 +784,13 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_split_kernel(Spli
     const float4 qo4 = *reinterpret_cast<const float4*>(&sm.qo[g][0]);
     const float qov[kHB] = {qo4.x, qo4.y, qo4.z, qo4.w};
     const float s1k = h2f(d.km & 0xffffu), s2k = h2f(d.km >> 16);
-    const float s1v = h2f(d.vm & 0xffffu), s2v = h2f(d.vm >> 16);
+    s1v = h2f(d.vm & 0xffffu);
+    s2v = h2f(d.vm >> 16);
     if (more) load_meta<M>(d, kmrow + tn * kTile, vmrow + tn * kTile, lane);
     const float ks = qscale * s1k;
-    float s[kHB];
 #pragma unroll
     for (int h = 0; h < kHB; ++h) s[h] = ks * fmaf(s2k, dot[h], qov[h]);
+    }
     // -- running max, raised only when a score exceeds it
     bool raised = false;
     float fl = 1.f;
@@ -719,7 +993,10 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParam
 template <int M, int G>
 hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s) {
   dim3 grid(a.n_split > 0 ? a.n_split : 1, a.Hkv * sp.hblocks, a.B);
-  hipLaunchKernelGGL((attn_split_kernel<M, G>), grid, dim3(kThreads), 0, s, sp);
+  if (a.rope)
+    hipLaunchKernelGGL((attn_split_kernel<M, G, true>), grid, dim3(kThreads), 0, s, sp);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<M, G, false>), grid, dim3(kThreads), 0, s, sp);
   return hipGetLastError();
 }
 
@@ -757,7 +1034,7 @@ hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s) {
   SplitParams sp{a.q,     a.kc,       a.vc,    a.km,      a.vm,      a.ks,    a.vs,
                  a.kr,    a.vr,       static_cast<const uint8_t*>(a.table), a.work,
                  a.Hq,    a.Hkv,      grp,     hblocks,   a.n_quant, a.n_split, a.chunk,
-                 a.n_resid, a.cap,    a.rcap,  a.scale};
+                 a.n_resid, a.cap,    a.rcap,  a.scale,   a.q_pos,   a.rope_base};
   hipError_t e;
   if (a.sub_dim == 4)
     e = a.group_size == 128 ? split_launch<4, 128>(a, sp, s) : split_launch<4, 256>(a, sp, s);

@@ -6,6 +6,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <cmath>
+
 #include "nsn.h"
 #include "nsn_device.h"
 #include "nsn_launch.h"
@@ -273,12 +275,14 @@ size_t nsn_decode_attention_workspace_size(const nsn_params* p, const nsn_attn_s
   return nsn::attn_workspace_bytes(s->batch, s->n_q_heads, n_split);
 }
 
-nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s, const uint16_t* q,
-                                const uint8_t* k_codes, const uint16_t* k_meta,
-                                const uint16_t* k_shift, const uint8_t* v_codes,
-                                const uint16_t* v_meta, const uint16_t* v_shift,
-                                const uint16_t* k_resid, const uint16_t* v_resid, const void* table,
-                                void* workspace, size_t workspace_bytes, float* out, void* stream) {
+static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shape* s,
+                                        const nsn_rope* r, const uint16_t* q,
+                                        const uint8_t* k_codes, const uint16_t* k_meta,
+                                        const uint16_t* k_shift, const uint8_t* v_codes,
+                                        const uint16_t* v_meta, const uint16_t* v_shift,
+                                        const uint16_t* k_resid, const uint16_t* v_resid,
+                                        const void* table, void* workspace, size_t workspace_bytes,
+                                        float* out, void* stream, const char* what) {
   NSN_TRY(check_attn(p, s));
   if (!q || !table || !workspace || !out)
     return fail(NSN_ERR_INVALID_ARG, "q, table, workspace and out must be non-NULL");
@@ -321,8 +325,39 @@ nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s, co
   a.out = out;
   a.n_split = n_split;
   a.chunk = chunk;
-  return hip_status(nsn::launch_decode_attention(a, static_cast<hipStream_t>(stream)),
-                    "nsn_decode_attention launch");
+  a.rope = r ? 1 : 0;
+  a.rope_base = r ? r->base : 0.f;
+  a.q_pos = r ? r->q_pos : 0;
+  return hip_status(nsn::launch_decode_attention(a, static_cast<hipStream_t>(stream)), what);
+}
+
+nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s, const uint16_t* q,
+                                const uint8_t* k_codes, const uint16_t* k_meta,
+                                const uint16_t* k_shift, const uint8_t* v_codes,
+                                const uint16_t* v_meta, const uint16_t* v_shift,
+                                const uint16_t* k_resid, const uint16_t* v_resid, const void* table,
+                                void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  return decode_attention_impl(p, s, nullptr, q, k_codes, k_meta, k_shift, v_codes, v_meta, v_shift,
+                               k_resid, v_resid, table, workspace, workspace_bytes, out, stream,
+                               "nsn_decode_attention launch");
+}
+
+nsn_status nsn_decode_attention_rope(const nsn_params* p, const nsn_attn_shape* s,
+                                     const nsn_rope* r, const uint16_t* q,
+                                     const uint8_t* k_codes, const uint16_t* k_meta,
+                                     const uint16_t* k_shift, const uint8_t* v_codes,
+                                     const uint16_t* v_meta, const uint16_t* v_shift,
+                                     const uint16_t* k_resid, const uint16_t* v_resid,
+                                     const void* table, void* workspace, size_t workspace_bytes,
+                                     float* out, void* stream) {
+  if (!r) return fail(NSN_ERR_INVALID_ARG, "rope must be non-NULL");
+  if (!(r->base > 1.0f) || !std::isfinite(r->base))
+    return fail(NSN_ERR_INVALID_ARG, "rope base must be finite and > 1, got %g", static_cast<double>(r->base));
+  if (r->q_pos < 0 || r->q_pos > (int64_t(1) << 40))
+    return fail(NSN_ERR_INVALID_ARG, "q_pos must lie in [0, 2^40], got %lld", static_cast<long long>(r->q_pos));
+  return decode_attention_impl(p, s, r, q, k_codes, k_meta, k_shift, v_codes, v_meta, v_shift,
+                               k_resid, v_resid, table, workspace, workspace_bytes, out, stream,
+                               "nsn_decode_attention_rope launch");
 }
 
 }  // extern "C"

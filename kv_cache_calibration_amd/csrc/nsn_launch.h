@@ -70,6 +70,9 @@ struct AttnArgs {
   float* out;
   int n_split;   // chunks per (b, kv-head block)
   int chunk;     // quantized tokens per chunk (multiple of group_size)
+  int rope;          // 1: keys are stored before rotary embedding
+  float rope_base;   // rotary base (rope = 1)
+  int64_t q_pos;     // query position (rope = 1)
 };
 // Split choice shared by the workspace-size query and the launch.
 void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size,

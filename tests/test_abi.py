@@ -170,6 +170,30 @@ def test_attention_workspace_size_and_check(lib):
     assert st == _lib.NSN_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("q_pos,base,status", [
+    (10, 1.0, _lib.NSN_ERR_INVALID_ARG),            # base must exceed 1
+    (10, float("inf"), _lib.NSN_ERR_INVALID_ARG),
+    (10, float("nan"), _lib.NSN_ERR_INVALID_ARG),
+    (-1, 10000.0, _lib.NSN_ERR_INVALID_ARG),        # negative position
+    ((1 << 40) + 1, 10000.0, _lib.NSN_ERR_INVALID_ARG),
+])
+def test_attention_rope_validation(lib, q_pos, base, status):
+    s = _shape()
+    r = _lib.nsn_rope(q_pos, base)
+    args = [FAKE] * 10
+    st = lib.nsn_decode_attention_rope(P(), ctypes.byref(s), ctypes.byref(r), *args, FAKE, 1 << 30,
+                                       FAKE, NULL)
+    assert st == status
+    st = lib.nsn_decode_attention_rope(P(), ctypes.byref(s), None, *args, FAKE, 1 << 30, FAKE, NULL)
+    assert st == _lib.NSN_ERR_INVALID_ARG
+    # the shape checks are those of nsn_decode_attention
+    bad = _shape(n_quant_tok=1000)
+    ok = _lib.nsn_rope(10, 10000.0)
+    st = lib.nsn_decode_attention_rope(P(), ctypes.byref(bad), ctypes.byref(ok), *args, FAKE,
+                                       1 << 30, FAKE, NULL)
+    assert st == _lib.NSN_ERR_INVALID_ARG
+
+
 def test_binding_inner_layout_checks():
     torch = pytest.importorskip("torch")
     import kv_cache_calibration_amd as nsnq
