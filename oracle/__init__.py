@@ -48,3 +48,11 @@ from .attention import (  # noqa: F401
     decode_attention_rope,
     decode_attention_rotated,
 )
+from .dq import (  # noqa: F401
+    codebook_4bit,
+    dq_decode_group,
+    dq_encode_group,
+    dq_pack,
+    dq_unpack,
+    record_bytes,
+)
