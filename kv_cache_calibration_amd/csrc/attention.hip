@@ -634,12 +634,29 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
 
   TileData<M> d;
   HOps ho{};
+  // rotary path: key codes of keys t32 and 32 + t32 of the tile, and this
+  // lane's word (channels 2 lane, 2 lane + 1) of the tile's group shift,
+  // fetched one tile ahead
+  u32x4 kpre[2][CB / 16];
+  uint32_t opre = 0;
+  auto load_rope = [&](int tile) {
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int i = 0; i < CB / 16; ++i)
+        kpre[ht][i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(kcrow + (tile * kTile + 32 * ht + (lane & 31)) * CB) + i);
+    opre = reinterpret_cast<const uint32_t*>(ksg + static_cast<int64_t>(tile / TPG) * kD)[lane];
+  };
   if constexpr (ROPE) ho = hadamard_ops(lane);
   for (int tau = wave; tau < ntiles; tau += kWaves) {
     const int tn = tau + kWaves;
     const bool more = tn < ntiles;
     if (tau == wave) {
-      if constexpr (!ROPE) load_keys<M>(d, kcrow + tau * kTile * CB, koff);
+      if constexpr (ROPE)
+        load_rope(tau);
+      else
+        load_keys<M>(d, kcrow + tau * kTile * CB, koff);
       load_meta<M>(d, kmrow + tau * kTile, vmrow + tau * kTile, lane);
       load_values<M>(d, vcrow + tau * kTile * CB, voff);
     }
@@ -650,8 +667,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       // lane holding channels 2 lane, 2 lane + 1; the queries turned to the
       // tile's first position
       {
-        const uint32_t ww = reinterpret_cast<const uint32_t*>(ksg + static_cast<int64_t>(tau / TPG) * kD)[lane];
-        float x0 = h2f(ww & 0xffffu), x1 = h2f(ww >> 16);
+        float x0 = h2f(opre & 0xffffu), x1 = h2f(opre >> 16);
         const float u0 = x0 + x1, u1 = x0 - x1;
         x0 = u0;
         x1 = u1;
@@ -677,11 +693,10 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
 #pragma unroll
       for (int ht = 0; ht < 2; ++ht) {
         const int tok = 32 * ht + t32;   // key of the tile
-        const uint8_t* kt = kcrow + (tau * kTile + tok) * CB;
         u32x4 xv[8];   // channels 16kb + 8hf .. + 7 of the key, codewords (fp16, exact)
         if constexpr (M == 4) {
-          const u32x4 w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt));
-          const u32x4 w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt) + 1);
+          const u32x4 w0 = kpre[ht][0];
+          const u32x4 w1 = kpre[ht][CB / 16 - 1];
           const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
@@ -693,7 +708,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
             xv[kb] = u32x4{a0.x, a0.y, a1.x, a1.y};
           }
         } else {
-          const u32x4 w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt));
+          const u32x4 w0 = kpre[ht][0];
           const uint32_t ww[4] = {w0.x, w0.y, w0.z, w0.w};
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) {
@@ -703,11 +718,12 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
           }
         }
         // k = s1 (s2' H c / sqrt(d) + og), turned by the key's offset, dotted
-        // with the turned queries over this lane's 64 channels; row blocks
-        // (pm, pm + 2) hold the pairs (c, c + 64) of channels 32pm ..
+        // with the turned queries over this lane's 64 channels (s1 applied to
+        // the sum); row blocks (pm, pm + 2) hold the pairs (c, c + 64) of
+        // channels 32pm ..
         const uint32_t kmt = __shfl(d.km, tok, kWave);
         const float s1k = h2f(kmt & 0xffffu), s2k = h2f(kmt >> 16);
-        const float a = s1k * s2k * kInvSqrtD;
+        const float a = s2k * kInvSqrtD;
         float part[kHB] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pm = 0; pm < 2; ++pm) {
@@ -735,8 +751,8 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g4 + e;
               const float2 cs = rsm.tab[cb0 + e][tok];
-              const float x = fmaf(a, hx[r], s1k * oxv[e]);
-              const float y = fmaf(a, hy[r], s1k * oyv[e]);
+              const float x = fmaf(a, hx[r], oxv[e]);
+              const float y = fmaf(a, hy[r], oyv[e]);
               const float kx = x * cs.x - y * cs.y;
               const float ky = y * cs.x + x * cs.y;
 #pragma unroll
@@ -747,13 +763,14 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
         }
 #pragma unroll
         for (int h = 0; h < kHB; ++h) {
-          const float v = half_pair_sum(part[h]);
+          const float v = half_pair_sum(part[h]) * s1k;
           sh[h] = ht == hf ? v : sh[h];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int h = 0; h < kHB; ++h) s[h] = sh[h] * qscale;
+      if (more) load_rope(tn);
       s1v = h2f(d.vm & 0xffffu);
       s2v = h2f(d.vm >> 16);
       if (more) load_meta<M>(d, kmrow + tn * kTile, vmrow + tn * kTile, lane);
