@@ -54,12 +54,43 @@ typedef enum { NSN_F16 = 0, NSN_F32 = 1 } nsn_dtype;
  * original vector is preserved; folded into the stored s2). */
 #define NSN_SCALE_ADJUST 1u
 
+/* nsn_params.flags: double quantization (NSNQuant summary, §3, Double
+ * Quantization: the NSN byproducts s1 and o, and the codebook entries, are
+ * themselves stored at 4 bits).  The pages fix no grids; this library reads
+ * them as follows.  Requires group_size 128 (else NSN_ERR_UNSUPPORTED).
+ *   meta   one fp16 s2' per token (s1 moves into the group record):
+ *          meta + s*meta_seq_stride + t.
+ *   shift  one record of 136 bytes (68 uint16) per group of 128 tokens, at
+ *          shift + s*shift_seq_stride + (t/128)*68:
+ *            bytes 0..7    fp16 lo, hi (min and max of the group's s1),
+ *                          fp16 sc = max |o'| / 7, fp16 0;
+ *            bytes 8..71   o' codes, channel c in byte 8 + c/2 (low nibble
+ *                          for even c): round(o'_c / sc) clamped to [-7, 7]
+ *                          plus 8; 0 when sc == 0; decodes to (code-8)*sc,
+ *                          a code of 0 to 0;
+ *            bytes 72..135 s1 codes, token t of the group in byte 72 + t/2
+ *                          likewise: round((s1 - lo) * 15 / (hi - lo))
+ *                          clamped to [0, 15], 0 when hi == lo; decodes to
+ *                          lo + code * (hi - lo) / 15.
+ *          Codes are decided in fp32, round half to even, from the
+ *          unrounded s1 and o'.
+ *   codebook  nsn_prepare_codebook rounds every entry to the nearest of the
+ *          16 levels (k - 7.5) * 3/8, k = 0..15 (ties to the smaller
+ *          magnitude, an entry of 0 to +3/16); the search, dequantization
+ *          and attention use the rounded codebook.
+ * nsn_quantize with this flag takes fp16 input only.  Dequantization and
+ * nsn_decode_attention take the decoded values as exact;
+ * nsn_decode_attention_rope does not support the flag.  Metadata cost:
+ * (2 + 136/128) bytes per token, 0.19 bits per value against 0.375 for
+ * the fp16 (s1, s2', o') layout. */
+#define NSN_DQ 2u
+
 typedef struct {
   int32_t head_dim;   /* d: must be 128 */
   int32_t sub_dim;    /* m: 4 (2-bit codes) or 8 (1-bit codes) */
   int32_t n_codes;    /* K: must be 256 (one byte per code) */
   int32_t group_size; /* G: tokens per Shift group; 128 or 256 */
-  uint32_t flags;     /* NSN_SCALE_ADJUST or 0 */
+  uint32_t flags;     /* NSN_SCALE_ADJUST | NSN_DQ, or 0 */
 } nsn_params;
 
 /* Size in bytes of a prepared codebook for these params (codebook, squared
@@ -135,6 +166,9 @@ nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table,
  *          NSN_SCALE_ADJUST).
  *   shift  fp16 [128] at shift + s*shift_seq_stride + (t/G)*128: the group's
  *          channel mean o, stored rotated (H o / sqrt(128)).
+ *   With NSN_DQ, meta and shift hold the layouts given at that flag; the
+ *   strides are then at least n_tok and (n_tok/128)*68 (multiples of 8 and
+ *   4), and in_dtype must be NSN_F16.
  * Strides let a flush write into a preallocated cache at a group offset:
  * pass pointers advanced to the offset and the cache's sequence strides.
  */
@@ -202,8 +236,11 @@ typedef struct {
  *
  * q        device fp16 [B][Hq][128].
  * k_codes, v_codes   device uint8 [B][Hkv][cache_capacity][128/m].
- * k_meta,  v_meta    device fp16  [B][Hkv][cache_capacity][2].
- * k_shift, v_shift   device fp16  [B][Hkv][cache_capacity/G][128].
+ * k_meta,  v_meta    device fp16  [B][Hkv][cache_capacity][2]
+ *                    (NSN_DQ: [B][Hkv][cache_capacity], s2' only).
+ * k_shift, v_shift   device fp16  [B][Hkv][cache_capacity/G][128]
+ *                    (NSN_DQ: uint16 [B][Hkv][cache_capacity/128][68], the
+ *                    group records).
  * k_resid, v_resid   device fp16  [B][Hkv][resid_capacity][128].
  * workspace          device, >= nsn_decode_attention_workspace_size().
  * out      device fp32 [B][Hq][128].
@@ -238,7 +275,7 @@ nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s,
  * for nsn_decode_attention.
  *
  * rope     host; base finite and > 1, 0 <= q_pos <= 2^40, else
- *          NSN_ERR_INVALID_ARG.
+ *          NSN_ERR_INVALID_ARG.  NSN_DQ gives NSN_ERR_UNSUPPORTED.
  */
 typedef struct {
   int64_t q_pos;   /* position of the query token */

@@ -12,12 +12,16 @@ must be contiguous):
     meta    (n_seq, cap, 2)                fp16   (s1, s2')
     shift   (n_seq, cap // G, 128)         fp16   rotated group mean
     table   (nsn_table_size,)              uint8  prepared codebook
+With double quantization (``Params(dq=True)``, NSN_DQ, G = 128):
+    meta    (n_seq, cap)                   fp16   s2'
+    shift   (n_seq, cap // 128, 136)       uint8  group records
+            (any 2-byte-aligned dtype works; strides are passed in bytes / 2)
 """
 
 import ctypes
 
 from . import _lib
-from ._lib import NSN_SCALE_ADJUST, NsnError  # noqa: F401
+from ._lib import NSN_DQ, NSN_SCALE_ADJUST, NsnError  # noqa: F401
 
 __all__ = [
     "Params",
@@ -43,9 +47,10 @@ def lib_path():
 class Params:
     """Python view of ``nsn_params``."""
 
-    def __init__(self, sub_dim=4, group_size=128, scale_adjust=True, head_dim=128, n_codes=256):
+    def __init__(self, sub_dim=4, group_size=128, scale_adjust=True, head_dim=128, n_codes=256,
+                 dq=False):
         self.c = _lib.nsn_params(head_dim, sub_dim, n_codes, group_size,
-                                 NSN_SCALE_ADJUST if scale_adjust else 0)
+                                 (NSN_SCALE_ADJUST if scale_adjust else 0) | (NSN_DQ if dq else 0))
 
     @property
     def sub_dim(self):
@@ -54,6 +59,15 @@ class Params:
     @property
     def group_size(self):
         return self.c.group_size
+
+    @property
+    def dq(self):
+        return bool(self.c.flags & NSN_DQ)
+
+
+def _stride16(t):
+    """dim-0 stride in 2-byte units (meta and shift strides of the C ABI)."""
+    return t.stride(0) * t.element_size() // 2
 
 
 def _ptr(t):
@@ -151,7 +165,7 @@ def nsn_quantize(params, x, table, codes, meta, shift, n_tok=None, stream=None):
     lib = _lib.load()
     _lib.check(lib.nsn_quantize(ctypes.byref(params.c), _dtype_code(x), _ptr(x), x.shape[0], n_tok,
                                 x.stride(0), _ptr(table), _ptr(codes), codes.stride(0), _ptr(meta),
-                                meta.stride(0), _ptr(shift), shift.stride(0), _stream(stream)))
+                                _stride16(meta), _ptr(shift), _stride16(shift), _stream(stream)))
 
 
 def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=None):
@@ -160,7 +174,7 @@ def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=No
     _inner_contig(out, (out.shape[1], 128))
     lib = _lib.load()
     _lib.check(lib.nsn_dequantize(ctypes.byref(params.c), _ptr(codes), codes.stride(0), _ptr(meta),
-                                  meta.stride(0), _ptr(shift), shift.stride(0), _ptr(table),
+                                  _stride16(meta), _ptr(shift), _stride16(shift), _ptr(table),
                                   out.shape[0], n_tok, _dtype_code(out), _ptr(out), out.stride(0),
                                   _stream(stream)))
 

@@ -18,6 +18,7 @@ NSN_ERR_HIP = 4
 NSN_F16 = 0
 NSN_F32 = 1
 NSN_SCALE_ADJUST = 1
+NSN_DQ = 2
 
 
 class nsn_params(ctypes.Structure):

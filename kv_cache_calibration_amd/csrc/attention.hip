@@ -119,6 +119,13 @@ struct RopeSmem {
 struct NoRopeSmem {
   int unused;
 };
+// Double-quantized metadata: per group of the chunk, (lo, step) of the s1
+// grid of keys and of values, and the value shift's scale.
+struct DqSmem {
+  float2 kls[kMaxGroups];
+  float2 vls[kMaxGroups];
+  float vsc[kMaxGroups];
+};
 
 // ds_read_b64_tr_b16: inside each group of 16 lanes, lane 4a + b receives
 // element b of the 8-byte chunks addressed by lanes 4k + a, k = 0..3.  With
@@ -489,12 +496,20 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, RopeSmem* rs, d
   }
 }
 
-template <int M, int G, bool ROPE>
+// DQ: meta holds one fp16 s2' per token, the shift arrays hold the group
+// records of the double quantization (4-bit s1 and o', decoded on the fly:
+// o' into <q', o'> at set-up and into the value shift at the end, s1 with
+// each tile's metadata).
+template <int M, int G, bool ROPE, bool DQ>
 __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_kernel(SplitParams p) {
+  static_assert(!(ROPE && DQ), "rotary keys with double quantization are not supported");
+  static_assert(!DQ || G == 128, "double quantization uses groups of 128");
   constexpr int CB = kD / M;            // code bytes per token
   constexpr int TPG = G / kTile;        // tiles per group
+  constexpr int RB = 2 * kDqRecU16;     // record bytes
   __shared__ AttnSmem<M> smem;
   __shared__ std::conditional_t<ROPE, RopeSmem, NoRopeSmem> rsm;
+  __shared__ std::conditional_t<DQ, DqSmem, NoRopeSmem> dsm;
   SplitSmem<M>& sm = smem.s;
 
   const int tid = threadIdx.x;
@@ -536,6 +551,8 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
   const int64_t row = static_cast<int64_t>(b) * p.Hkv + kvh;  // (b, kv head) cache row
   const uint16_t* ksg = p.ks + (row * (p.cap / G) + c0 / G) * kD;
   const uint16_t* vsg = p.vs + (row * (p.cap / G) + c0 / G) * kD;
+  const uint8_t* krec = reinterpret_cast<const uint8_t*>(p.ks + (row * (p.cap / G) + c0 / G) * kDqRecU16);
+  const uint8_t* vrec = reinterpret_cast<const uint8_t*>(p.vs + (row * (p.cap / G) + c0 / G) * kDqRecU16);
 
   // ---- set-up: fp16 codebook, rotated queries (wave = head), zero weight slots
   {
@@ -565,7 +582,34 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
   }
   __syncthreads();
   // <q'_h, o'_g> for every group of the chunk, one thread per (g, h)
-  for (int idx = tid; idx < (ROPE ? 0 : ng * kHB); idx += kThreads) {
+  if constexpr (DQ) {
+    for (int idx = tid; idx < ng * kHB; idx += kThreads) {
+      const int g = idx / kHB, h = idx % kHB;
+      const uint8_t* rec = krec + static_cast<int64_t>(g) * RB;
+      const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rec + 8);
+      float s = 0.f;
+#pragma unroll 4
+      for (int i = 0; i < kD / 8; ++i) {
+        const uint32_t w = w32[i];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = static_cast<int>((w >> (4 * k)) & 15u);
+          s = fmaf(sm.qr[h][8 * i + k], c ? static_cast<float>(c - 8) : 0.f, s);
+        }
+      }
+      sm.qo[g][h] = s * h2f(reinterpret_cast<const uint16_t*>(rec)[2]);
+    }
+    for (int g = tid; g < ng; g += kThreads) {
+      const uint2 kh = *reinterpret_cast<const uint2*>(krec + static_cast<int64_t>(g) * RB);
+      const uint2 vh = *reinterpret_cast<const uint2*>(vrec + static_cast<int64_t>(g) * RB);
+      const float klo = h2f(kh.x & 0xffffu), khi = h2f(kh.x >> 16);
+      const float vlo = h2f(vh.x & 0xffffu), vhi = h2f(vh.x >> 16);
+      dsm.kls[g] = make_float2(klo, dq_step(klo, khi));
+      dsm.vls[g] = make_float2(vlo, dq_step(vlo, vhi));
+      dsm.vsc[g] = h2f(vh.y & 0xffffu);
+    }
+  }
+  for (int idx = tid; idx < (ROPE || DQ ? 0 : ng * kHB); idx += kThreads) {
     const int g = idx / kHB, h = idx % kHB;
     const uint4* o = reinterpret_cast<const uint4*>(ksg + static_cast<int64_t>(g) * kD);
     float s = 0.f;
@@ -627,12 +671,38 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
   const uint8_t* vcrow = p.vc + row * p.cap * CB + static_cast<int64_t>(c0) * CB;
   const uint32_t* kmrow = reinterpret_cast<const uint32_t*>(p.km + row * p.cap * 2) + c0;
   const uint32_t* vmrow = reinterpret_cast<const uint32_t*>(p.vm + row * p.cap * 2) + c0;
+  const uint16_t* kmrow16 = p.km + row * p.cap + c0;   // DQ: s2' per token
+  const uint16_t* vmrow16 = p.vm + row * p.cap + c0;
   const uint32_t koff = c16 * CB + (M == 4 ? 8 : 4) * R;
   const uint32_t voff = (8 * R + k4) * CB + (M == 4 ? 8 : 4) * a4;
   const uint32_t cbh_base = lds_addr(sm.cbh);   // codebook copy of this lane
   const uint32_t wtr = lds_addr(&sm.wrow[wave][8 * R + k4][4 * a4]);
 
   TileData<M> d;
+  // metadata of token `lane` of a tile: (s1, s2') fp16 pair, or with DQ
+  // s2' in the low half and the 4-bit s1 code in bits 16..19
+  auto lmeta = [&](int tile) {
+    if constexpr (DQ) {
+      const int t = tile * kTile + lane;
+      const int64_t rb = static_cast<int64_t>(tile / TPG) * RB + 8 + kD / 2 + (t % G) / 2;
+      const int sh = 4 * (t & 1);
+      d.km = static_cast<uint32_t>(__builtin_nontemporal_load(kmrow16 + t)) | (((krec[rb] >> sh) & 15u) << 16);
+      d.vm = static_cast<uint32_t>(__builtin_nontemporal_load(vmrow16 + t)) | (((vrec[rb] >> sh) & 15u) << 16);
+    } else {
+      load_meta<M>(d, kmrow + tile * kTile, vmrow + tile * kTile, lane);
+    }
+  };
+  // (s1, s2') from a metadata word of tile `tile`'s group
+  auto umeta = [&](uint32_t w, int tile, bool is_v, float& s1, float& s2) {
+    if constexpr (DQ) {
+      const float2 ls = is_v ? dsm.vls[tile / TPG] : dsm.kls[tile / TPG];
+      s1 = dq_s1(w >> 16, ls.x, ls.y);
+      s2 = h2f(w & 0xffffu);
+    } else {
+      s1 = h2f(w & 0xffffu);
+      s2 = h2f(w >> 16);
+    }
+  };
   HOps ho{};
   // rotary path: key codes of keys t32 and 32 + t32 of the tile, and this
   // lane's word (channels 2 lane, 2 lane + 1) of the tile's group shift,
@@ -657,7 +727,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
         load_rope(tau);
       else
         load_keys<M>(d, kcrow + tau * kTile * CB, koff);
-      load_meta<M>(d, kmrow + tau * kTile, vmrow + tau * kTile, lane);
+      lmeta(tau);
       load_values<M>(d, vcrow + tau * kTile * CB, voff);
     }
     float s[kHB];
@@ -771,9 +841,8 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
 #pragma unroll
       for (int h = 0; h < kHB; ++h) s[h] = sh[h] * qscale;
       if (more) load_rope(tn);
-      s1v = h2f(d.vm & 0xffffu);
-      s2v = h2f(d.vm >> 16);
-      if (more) load_meta<M>(d, kmrow + tn * kTile, vmrow + tn * kTile, lane);
+      umeta(d.vm, tau, true, s1v, s2v);
+      if (more) lmeta(tn);
     } else {
     // -- scores
     v4f sacc[4];
@@ -800,10 +869,10 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
     const int g = tau / TPG;
     const float4 qo4 = *reinterpret_cast<const float4*>(&sm.qo[g][0]);
     const float qov[kHB] = {qo4.x, qo4.y, qo4.z, qo4.w};
-    const float s1k = h2f(d.km & 0xffffu), s2k = h2f(d.km >> 16);
-    s1v = h2f(d.vm & 0xffffu);
-    s2v = h2f(d.vm >> 16);
-    if (more) load_meta<M>(d, kmrow + tn * kTile, vmrow + tn * kTile, lane);
+    float s1k, s2k;
+    umeta(d.km, tau, false, s1k, s2k);
+    umeta(d.vm, tau, true, s1v, s2v);
+    if (more) lmeta(tn);
     const float ks = qscale * s1k;
 #pragma unroll
     for (int h = 0; h < kHB; ++h) s[h] = ks * fmaf(s2k, dot[h], qov[h]);
@@ -940,8 +1009,14 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       a = fmaf(e, reinterpret_cast<const float*>(&sm.wrow[w][0][0])[h * kD + c], a);
       l = fmaf(e, sm.wl[w][h], l);
     }
+    if constexpr (DQ) {
 #pragma unroll 8
-    for (int g = 0; g < ng; ++g) a = fmaf(sm.sg[g][h], h2f(vsg[static_cast<int64_t>(g) * kD + c]), a);
+      for (int g = 0; g < ng; ++g)
+        a = fmaf(sm.sg[g][h], dq_nibble_o(vrec[static_cast<int64_t>(g) * RB + 8 + c / 2], c & 1, dsm.vsc[g]), a);
+    } else {
+#pragma unroll 8
+      for (int g = 0; g < ng; ++g) a = fmaf(sm.sg[g][h], h2f(vsg[static_cast<int64_t>(g) * kD + c]), a);
+    }
     if (h < nh) {
       float* dst = p.work + ((static_cast<int64_t>(b) * p.Hq + h0 + h) * (p.n_split + 1) + split) * kPartStride;
       dst[c] = a;
@@ -1010,10 +1085,18 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParam
 template <int M, int G>
 hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s) {
   dim3 grid(a.n_split > 0 ? a.n_split : 1, a.Hkv * sp.hblocks, a.B);
+  if (a.rope && a.dq) return hipErrorInvalidValue;
   if (a.rope)
-    hipLaunchKernelGGL((attn_split_kernel<M, G, true>), grid, dim3(kThreads), 0, s, sp);
-  else
-    hipLaunchKernelGGL((attn_split_kernel<M, G, false>), grid, dim3(kThreads), 0, s, sp);
+    hipLaunchKernelGGL((attn_split_kernel<M, G, true, false>), grid, dim3(kThreads), 0, s, sp);
+  else if constexpr (G == 128) {
+    if (a.dq)
+      hipLaunchKernelGGL((attn_split_kernel<M, G, false, true>), grid, dim3(kThreads), 0, s, sp);
+    else
+      hipLaunchKernelGGL((attn_split_kernel<M, G, false, false>), grid, dim3(kThreads), 0, s, sp);
+  } else {
+    if (a.dq) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_split_kernel<M, G, false, false>), grid, dim3(kThreads), 0, s, sp);
+  }
   return hipGetLastError();
 }
 

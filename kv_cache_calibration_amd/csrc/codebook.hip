@@ -100,8 +100,22 @@ __global__ void kmeans_finish(const double* __restrict__ cent, float* __restrict
   if (id < kCodes * M) out[id] = round_to_half(cent[id]);
 }
 
+// Nearest of the 16 levels (k - 7.5) * 3/8 of the double-quantized codebook
+// [NSNQuant summary, Methodology §3, Double Quantization: codebook entries
+//  at 4 bits; the level grid is this library's reading].  Magnitude level
+// j (3/16 + 3j/8) owns |v| in (3j/8, 3(j+1)/8]; the bounds are exact in fp32,
+// so a tie goes to the smaller magnitude, and 0 goes to +3/16.
+__device__ __forceinline__ float level4(float v) {
+  const float a = fabsf(v);
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < 8; ++k) j = a > 0.375f * static_cast<float>(k) ? k : j;
+  const float m = 0.1875f + 0.375f * static_cast<float>(j);
+  return v < 0.f ? -m : m;
+}
+
 template <int M>
-__global__ void prepare_kernel(const float* __restrict__ cb, uint8_t* __restrict__ table) {
+__global__ void prepare_kernel(const float* __restrict__ cb, int dq, uint8_t* __restrict__ table) {
   const int k = threadIdx.x;  // 256 threads, one per codeword
   float* tc = reinterpret_cast<float*>(table + kTabCodebook);
   float* tn = reinterpret_cast<float*>(table + kTabNorm2);
@@ -109,7 +123,7 @@ __global__ void prepare_kernel(const float* __restrict__ cb, uint8_t* __restrict
   float n2 = 0.f;
 #pragma unroll
   for (int e = 0; e < M; ++e) {
-    const float c = cb[k * M + e];
+    const float c = dq ? level4(cb[k * M + e]) : cb[k * M + e];
     tc[k * M + e] = c;
     th[k * M + e] = f2h(c);
     n2 = fmaf(c, c, n2);
@@ -151,16 +165,16 @@ hipError_t launch_build_codebook(int sub_dim, int n_codes, int64_t n, int iters,
                       : build<8>(n, iters, samples, codebook, ws, s);
 }
 
-hipError_t launch_prepare_codebook(const float* codebook, int sub_dim, void* table,
+hipError_t launch_prepare_codebook(const float* codebook, int sub_dim, int dq, void* table,
                                    hipStream_t s) {
   uint8_t* t = static_cast<uint8_t*>(table);
   if (sub_dim == 4) {
-    hipLaunchKernelGGL(prepare_kernel<4>, dim3(1), dim3(256), 0, s, codebook, t);
+    hipLaunchKernelGGL(prepare_kernel<4>, dim3(1), dim3(256), 0, s, codebook, dq, t);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_search_table(table, s);
   }
-  hipLaunchKernelGGL(prepare_kernel<8>, dim3(1), dim3(256), 0, s, codebook, t);
+  hipLaunchKernelGGL(prepare_kernel<8>, dim3(1), dim3(256), 0, s, codebook, dq, t);
   return hipGetLastError();
 }
 

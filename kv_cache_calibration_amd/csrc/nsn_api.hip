@@ -46,7 +46,9 @@ nsn_status check_params(const nsn_params* p) {
   if (p->n_codes != 256) return fail(NSN_ERR_UNSUPPORTED, "n_codes must be 256 (got %d)", p->n_codes);
   if (p->group_size != 128 && p->group_size != 256)
     return fail(NSN_ERR_UNSUPPORTED, "group_size must be 128 or 256 (got %d)", p->group_size);
-  if (p->flags & ~NSN_SCALE_ADJUST) return fail(NSN_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(NSN_SCALE_ADJUST | NSN_DQ)) return fail(NSN_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
+  if ((p->flags & NSN_DQ) && p->group_size != 128)
+    return fail(NSN_ERR_UNSUPPORTED, "NSN_DQ needs group_size 128 (got %d)", p->group_size);
   return NSN_OK;
 }
 
@@ -115,7 +117,7 @@ nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook, void
     return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   if (table_bytes < nsn::kTabBytes)
     return fail(NSN_ERR_WORKSPACE, "table needs %zu bytes, got %zu", nsn::kTabBytes, table_bytes);
-  return hip_status(nsn::launch_prepare_codebook(codebook, p->sub_dim, table,
+  return hip_status(nsn::launch_prepare_codebook(codebook, p->sub_dim, (p->flags & NSN_DQ) ? 1 : 0, table,
                                                  static_cast<hipStream_t>(stream)),
                     "nsn_prepare_codebook launch");
 }
@@ -137,6 +139,26 @@ nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table, const fl
                     "nsn_nearest_codeword launch");
 }
 
+// Sequence strides of meta and shift (uint16 units) for the plain and the
+// double-quantized layouts.
+static nsn_status check_meta_strides(const nsn_params* p, int64_t n_tok, int64_t meta_seq_stride,
+                                     int64_t shift_seq_stride) {
+  const int64_t G = p->group_size;
+  if (p->flags & NSN_DQ) {
+    if (meta_seq_stride < n_tok || meta_seq_stride % 8)
+      return fail(NSN_ERR_INVALID_ARG, "meta_seq_stride must be >= n_tok and a multiple of 8 (NSN_DQ)");
+    if (shift_seq_stride < (n_tok / G) * nsn::kDqRecU16 || shift_seq_stride % 4)
+      return fail(NSN_ERR_INVALID_ARG, "shift_seq_stride must be >= (n_tok/128)*%d and a multiple of 4 (NSN_DQ)",
+                  nsn::kDqRecU16);
+    return NSN_OK;
+  }
+  if (meta_seq_stride < n_tok * 2 || meta_seq_stride % 8)
+    return fail(NSN_ERR_INVALID_ARG, "meta_seq_stride must be >= 2*n_tok and a multiple of 8");
+  if (shift_seq_stride < (n_tok / G) * 128 || shift_seq_stride % 8)
+    return fail(NSN_ERR_INVALID_ARG, "shift_seq_stride must be >= (n_tok/G)*128 and a multiple of 8");
+  return NSN_OK;
+}
+
 nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype, const void* x, int64_t n_seq,
                         int64_t n_tok, int64_t x_seq_stride, const void* table, uint8_t* codes,
                         int64_t codes_seq_stride, uint16_t* meta, int64_t meta_seq_stride,
@@ -144,6 +166,8 @@ nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype, const void* x, 
   NSN_TRY(check_params(p));
   if (in_dtype != NSN_F16 && in_dtype != NSN_F32)
     return fail(NSN_ERR_INVALID_ARG, "in_dtype must be NSN_F16 or NSN_F32");
+  if ((p->flags & NSN_DQ) && in_dtype != NSN_F16)
+    return fail(NSN_ERR_UNSUPPORTED, "NSN_DQ quantizes fp16 input only");
   if (n_seq < 0 || n_tok < 0) return fail(NSN_ERR_INVALID_ARG, "n_seq and n_tok must be >= 0");
   if (n_tok % p->group_size)
     return fail(NSN_ERR_INVALID_ARG, "n_tok (%lld) must be a multiple of group_size (%d)",
@@ -164,16 +188,14 @@ nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype, const void* x, 
     if (codes_seq_stride < n_tok * nsub || codes_seq_stride % 16)
       return fail(NSN_ERR_INVALID_ARG, "codes_seq_stride must be >= n_tok*%lld and a multiple of 16",
                   static_cast<long long>(nsub));
-    if (meta_seq_stride < n_tok * 2 || meta_seq_stride % 8)
-      return fail(NSN_ERR_INVALID_ARG, "meta_seq_stride must be >= 2*n_tok and a multiple of 8");
-    if (shift_seq_stride < (n_tok / G) * 128 || shift_seq_stride % 8)
-      return fail(NSN_ERR_INVALID_ARG, "shift_seq_stride must be >= (n_tok/G)*128 and a multiple of 8");
+    NSN_TRY(check_meta_strides(p, n_tok, meta_seq_stride, shift_seq_stride));
   }
   if (n_seq * (n_tok / G) > 0x7fffffffLL)
     return fail(NSN_ERR_UNSUPPORTED, "too many token groups in one call");
   nsn::QuantArgs a{x, in_dtype == NSN_F32, n_seq, n_tok, x_seq_stride, table, codes,
                    codes_seq_stride, meta, meta_seq_stride, shift, shift_seq_stride,
-                   p->sub_dim, p->group_size, static_cast<int>(p->flags & NSN_SCALE_ADJUST)};
+                   p->sub_dim, p->group_size, static_cast<int>(p->flags & NSN_SCALE_ADJUST),
+                   (p->flags & NSN_DQ) ? 1 : 0};
   return hip_status(nsn::launch_quantize(a, static_cast<hipStream_t>(stream)), "nsn_quantize launch");
 }
 
@@ -204,16 +226,13 @@ nsn_status nsn_dequantize(const nsn_params* p, const uint8_t* codes, int64_t cod
     if (codes_seq_stride < n_tok * nsub || codes_seq_stride % 16)
       return fail(NSN_ERR_INVALID_ARG, "codes_seq_stride must be >= n_tok*%lld and a multiple of 16",
                   static_cast<long long>(nsub));
-    if (meta_seq_stride < n_tok * 2 || meta_seq_stride % 8)
-      return fail(NSN_ERR_INVALID_ARG, "meta_seq_stride must be >= 2*n_tok and a multiple of 8");
-    if (shift_seq_stride < (n_tok / G) * 128 || shift_seq_stride % 8)
-      return fail(NSN_ERR_INVALID_ARG, "shift_seq_stride must be >= (n_tok/G)*128 and a multiple of 8");
+    NSN_TRY(check_meta_strides(p, n_tok, meta_seq_stride, shift_seq_stride));
   }
   if (n_seq * (n_tok / G) > 0x7fffffffLL)
     return fail(NSN_ERR_UNSUPPORTED, "too many token groups in one call");
   nsn::DequantArgs a{codes, codes_seq_stride, meta, meta_seq_stride, shift, shift_seq_stride, table,
                      n_seq, n_tok, out_dtype == NSN_F32, x_hat, out_seq_stride, p->sub_dim,
-                     p->group_size};
+                     p->group_size, (p->flags & NSN_DQ) ? 1 : 0};
   return hip_status(nsn::launch_dequantize(a, static_cast<hipStream_t>(stream)),
                     "nsn_dequantize launch");
 }
@@ -328,6 +347,7 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
   a.rope = r ? 1 : 0;
   a.rope_base = r ? r->base : 0.f;
   a.q_pos = r ? r->q_pos : 0;
+  a.dq = (p->flags & NSN_DQ) ? 1 : 0;
   return hip_status(nsn::launch_decode_attention(a, static_cast<hipStream_t>(stream)), what);
 }
 
@@ -355,6 +375,8 @@ nsn_status nsn_decode_attention_rope(const nsn_params* p, const nsn_attn_shape* 
     return fail(NSN_ERR_INVALID_ARG, "rope base must be finite and > 1, got %g", static_cast<double>(r->base));
   if (r->q_pos < 0 || r->q_pos > (int64_t(1) << 40))
     return fail(NSN_ERR_INVALID_ARG, "q_pos must lie in [0, 2^40], got %lld", static_cast<long long>(r->q_pos));
+  if (p && (p->flags & NSN_DQ))
+    return fail(NSN_ERR_UNSUPPORTED, "NSN_DQ is not supported with rotary keys");
   return decode_attention_impl(p, s, r, q, k_codes, k_meta, k_shift, v_codes, v_meta, v_shift,
                                k_resid, v_resid, table, workspace, workspace_bytes, out, stream,
                                "nsn_decode_attention_rope launch");

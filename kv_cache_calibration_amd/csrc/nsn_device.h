@@ -130,6 +130,20 @@ __device__ __forceinline__ float wave_max_fast(float x) {
 __device__ __forceinline__ float wave_min_fast(float x) {
   return wave_allreduce_dpp(x, [](float a, float b) { return fminf(a, b); });
 }
+// Decoding of a double-quantized group record (4-bit codes, two per byte,
+// the low nibble first).  o': (code - 8) * sc, a code of 0 decodes to 0.
+// s1: lo + code * (hi - lo) / 15.
+__device__ __forceinline__ float dq_nibble_o(uint32_t byte, int high, float sc) {
+  const int c = static_cast<int>((byte >> (4 * high)) & 15u);
+  return c ? static_cast<float>(c - 8) * sc : 0.f;
+}
+__device__ __forceinline__ float dq_s1(uint32_t code, float lo, float step) {
+  return fmaf(static_cast<float>(code), step, lo);
+}
+__device__ __forceinline__ float dq_step(float lo, float hi) { return (hi - lo) / 15.0f; }
+__device__ __forceinline__ float dq_nibble_s1(uint32_t byte, int high, float lo, float hi) {
+  return dq_s1((byte >> (4 * high)) & 15u, lo, dq_step(lo, hi));
+}
 // x(lane) + x(lane ^ 32) on the VALU (permlane32 swap of x with itself
 // yields the lower half in one result and the upper half in the other).
 __device__ __forceinline__ float half_pair_sum(float x) {

@@ -8,6 +8,10 @@
 
 namespace nsn {
 
+// Double-quantized group record (G = 128): 8 header bytes, 64 bytes of o'
+// codes, 64 bytes of s1 codes, in uint16 units.
+constexpr int kDqRecU16 = 68;
+
 struct QuantArgs {
   const void* x;
   int in_f32;
@@ -20,6 +24,7 @@ struct QuantArgs {
   uint16_t* shift;
   int64_t shift_seq_stride;
   int sub_dim, group_size, scale_adjust;
+  int dq;   // 1: double-quantized metadata (meta = s2' per token, shift = group records)
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 bool quantize_mfma_supported(int in_f32, int sub_dim, int group_size);
@@ -41,10 +46,11 @@ struct DequantArgs {
   void* out;
   int64_t out_seq_stride;
   int sub_dim, group_size;
+  int dq;   // 1: double-quantized metadata
 };
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 
-hipError_t launch_prepare_codebook(const float* codebook, int sub_dim,
+hipError_t launch_prepare_codebook(const float* codebook, int sub_dim, int dq,
                                    void* table, hipStream_t s);
 
 hipError_t launch_build_codebook(int sub_dim, int n_codes, int64_t n,
@@ -73,6 +79,7 @@ struct AttnArgs {
   int rope;          // 1: keys are stored before rotary embedding
   float rope_base;   // rotary base (rope = 1)
   int64_t q_pos;     // query position (rope = 1)
+  int dq;            // 1: double-quantized metadata (group_size 128)
 };
 // Split choice shared by the workspace-size query and the launch.
 void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size,

@@ -186,7 +186,9 @@ template <> __device__ __forceinline__ void store_row<__half>(__half* row, const
 
 // Dequantize [NSNQuant summary §1: the byproducts reconstruct the tensor;
 // §4: dequantization kernel]: x_hat = R [ s1 (s2' c + o') ], R = H/sqrt(d).
-template <typename TOut, int M, int G>
+// DQ: s1 and o' come from the group's 4-bit record (§3, Double
+// Quantization), s2' from the one-fp16-per-token meta.
+template <typename TOut, int M, int G, bool DQ>
 __global__ __launch_bounds__(G) void dequantize_kernel(
     const uint8_t* __restrict__ codes, int64_t codes_seq_stride,
     const uint16_t* __restrict__ meta, int64_t meta_seq_stride,
@@ -203,7 +205,21 @@ __global__ __launch_bounds__(G) void dequantize_kernel(
 
   const float* cbg = reinterpret_cast<const float*>(table + kTabCodebook);
   for (int i = tid; i < kCodes * M; i += G) cb[i] = cbg[i];
-  if (tid < kD) osh[tid] = h2f(shift[seq * shift_seq_stride + grp * kD + tid]);
+  float s1, s2;
+  if constexpr (DQ) {
+    static_assert(G == kD, "one thread per channel and per token");
+    const uint8_t* rec = reinterpret_cast<const uint8_t*>(shift + seq * shift_seq_stride + grp * kDqRecU16);
+    const uint2 hd = *reinterpret_cast<const uint2*>(rec);
+    osh[tid] = dq_nibble_o(rec[8 + tid / 2], tid & 1, h2f(static_cast<uint16_t>(hd.y & 0xffffu)));
+    s1 = dq_nibble_s1(rec[8 + kD / 2 + tid / 2], tid & 1, h2f(static_cast<uint16_t>(hd.x & 0xffffu)),
+                      h2f(static_cast<uint16_t>(hd.x >> 16)));
+    s2 = h2f(meta[seq * meta_seq_stride + tok]);
+  } else {
+    if (tid < kD) osh[tid] = h2f(shift[seq * shift_seq_stride + grp * kD + tid]);
+    const uint32_t mv = *reinterpret_cast<const uint32_t*>(meta + seq * meta_seq_stride + 2 * tok);
+    s1 = h2f(static_cast<uint16_t>(mv & 0xffffu));
+    s2 = h2f(static_cast<uint16_t>(mv >> 16));
+  }
 
   uint32_t packed[NSUB / 4];
   const uint4* csrc = reinterpret_cast<const uint4*>(codes + seq * codes_seq_stride + tok * NSUB);
@@ -215,9 +231,6 @@ __global__ __launch_bounds__(G) void dequantize_kernel(
     packed[4 * w + 2] = c.z;
     packed[4 * w + 3] = c.w;
   }
-  const uint32_t mv = *reinterpret_cast<const uint32_t*>(meta + seq * meta_seq_stride + 2 * tok);
-  const float s1 = h2f(static_cast<uint16_t>(mv & 0xffffu));
-  const float s2 = h2f(static_cast<uint16_t>(mv >> 16));
   __syncthreads();
 
   float v[kD];
@@ -244,11 +257,11 @@ hipError_t quant_launch(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename TOut, int M, int G>
+template <typename TOut, int M, int G, bool DQ = false>
 hipError_t dequant_launch(const DequantArgs& a, hipStream_t s) {
   const int64_t n_groups = a.n_tok / G;
   const int64_t blocks = a.n_seq * n_groups;
-  hipLaunchKernelGGL((dequantize_kernel<TOut, M, G>), dim3(static_cast<unsigned>(blocks)), dim3(G), 0, s,
+  hipLaunchKernelGGL((dequantize_kernel<TOut, M, G, DQ>), dim3(static_cast<unsigned>(blocks)), dim3(G), 0, s,
                      a.codes, a.codes_seq_stride, a.meta, a.meta_seq_stride, a.shift,
                      a.shift_seq_stride, static_cast<const uint8_t*>(a.table), n_groups,
                      static_cast<TOut*>(a.out), a.out_seq_stride);
@@ -261,6 +274,7 @@ hipError_t quant_g(const QuantArgs& a, hipStream_t s) {
 }
 template <typename TOut, int M>
 hipError_t dequant_g(const DequantArgs& a, hipStream_t s) {
+  if (a.dq) return a.group_size == 128 ? dequant_launch<TOut, M, 128, true>(a, s) : hipErrorInvalidValue;
   return a.group_size == 128 ? dequant_launch<TOut, M, 128>(a, s)
                              : dequant_launch<TOut, M, 256>(a, s);
 }
@@ -270,6 +284,7 @@ hipError_t dequant_g(const DequantArgs& a, hipStream_t s) {
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.n_seq == 0 || a.n_tok == 0) return hipSuccess;
   if (quantize_mfma_supported(a.in_f32, a.sub_dim, a.group_size)) return launch_quantize_mfma(a, s);
+  if (a.dq) return hipErrorInvalidValue;   // double quantization runs on the matrix-core kernels only
   if (a.in_f32) return a.sub_dim == 4 ? quant_g<float, 4>(a, s) : quant_g<float, 8>(a, s);
   return a.sub_dim == 4 ? quant_g<__half, 4>(a, s) : quant_g<__half, 8>(a, s);
 }

@@ -243,6 +243,70 @@ __device__ __forceinline__ void nsn_front(const __half* __restrict__ x, int64_t 
   s2 = sqrtf(ss2 * (1.0f / kD));
 }
 
+// Double quantization of the group's byproducts (flag NSN_DQ), written after
+// every token's s1 is in s1g: a record of 8 + 64 + 64 bytes per group --
+// fp16 (lo, hi) = min and max of s1, fp16 scale = max |o'| / 7, 0; the o'
+// codes (channel c in byte c / 2, low nibble for even c: round(o'/scale)
+// in [-7, 7] plus 8, 0 for a zero scale); the s1 codes (token t likewise:
+// round((s1 - lo) * 15 / (hi - lo)) in [0, 15], 0 when hi == lo).  Codes
+// are taken in fp32 with round-half-even.  Contains block barriers.
+// [NSNQuant summary, Methodology §3, Double Quantization: s1 and o at 4
+//  bits; grids and second-level scales are this library's reading.]
+struct DqSmem {
+  float s1g[kG];
+  uint16_t par[4];
+};
+__device__ __forceinline__ void write_dq_record(const float* osh, DqSmem& dq, uint8_t* rec) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  if (w == 0) {
+    const float a = dq.s1g[lane], b = dq.s1g[lane + kWave];
+    const float mn = wave_min_fast(fminf(a, b)), mx = wave_max_fast(fmaxf(a, b));
+    if (lane == 0) {
+      dq.par[0] = f2h(mn);
+      dq.par[1] = f2h(mx);
+    }
+  } else if (w == 1) {
+    const float m = wave_max_fast(fmaxf(fabsf(osh[lane]), fabsf(osh[lane + kWave])));
+    if (lane == 0) {
+      dq.par[2] = f2h(m / 7.0f);
+      dq.par[3] = 0;
+    }
+  }
+  __syncthreads();
+  const float lo = h2f(dq.par[0]), hi = h2f(dq.par[1]), sc = h2f(dq.par[2]);
+  if (tid < kD / 2) {
+    // o' codes of channels 2 tid, 2 tid + 1
+    uint32_t c[2] = {0u, 0u};
+    if (sc > 0.f) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float t = rintf(osh[2 * tid + e] / sc);
+        c[e] = static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(t, -7.f), 7.f)) + 8);
+      }
+    }
+    rec[8 + tid] = static_cast<uint8_t>(c[0] | (c[1] << 4));
+  } else if (tid < kD / 2 + kG / 2) {
+    // s1 codes of tokens 2k, 2k + 1
+    const int k = tid - kD / 2;
+    uint32_t c[2] = {0u, 0u};
+    if (hi > lo) {
+      const float inv = 15.0f / (hi - lo);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float t = rintf((dq.s1g[2 * k + e] - lo) * inv);
+        c[e] = static_cast<uint32_t>(fminf(fmaxf(t, 0.f), 15.f));
+      }
+    }
+    rec[8 + kD / 2 + k] = static_cast<uint8_t>(c[0] | (c[1] << 4));
+  } else if (tid == kD / 2 + kG / 2) {
+    *reinterpret_cast<uint2*>(rec) = make_uint2(static_cast<uint32_t>(dq.par[0]) | (static_cast<uint32_t>(dq.par[1]) << 16),
+                                                static_cast<uint32_t>(dq.par[2]));
+  }
+}
+static_assert(kDqRecU16 * 2 == 8 + kD / 2 + kG / 2, "record size");
+
+template <bool DQ>
 __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
     const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
     const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
@@ -459,12 +523,22 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   }
   *reinterpret_cast<u32x4*>(codes + seq * codes_seq_stride + tok * 32 + 16 * hf) =
       u32x4{pk[0], pk[1], pk[2], pk[3]};
-  if (hf == 0) {
-    const uint32_t mv = static_cast<uint32_t>(f2h(s1)) |
-                        (static_cast<uint32_t>(f2h(s2 * alpha)) << 16);
-    *reinterpret_cast<uint32_t*>(meta + seq * meta_seq_stride + 2 * tok) = mv;
+  if constexpr (DQ) {
+    __shared__ DqSmem dqs;
+    if (hf == 0) {
+      dqs.s1g[tg] = s1;
+      meta[seq * meta_seq_stride + tok] = f2h(s2 * alpha);
+    }
+    __syncthreads();
+    write_dq_record(fs.osh, dqs, reinterpret_cast<uint8_t*>(shift + seq * shift_seq_stride + grp * kDqRecU16));
+  } else {
+    if (hf == 0) {
+      const uint32_t mv = static_cast<uint32_t>(f2h(s1)) |
+                          (static_cast<uint32_t>(f2h(s2 * alpha)) << 16);
+      *reinterpret_cast<uint32_t*>(meta + seq * meta_seq_stride + 2 * tok) = mv;
+    }
+    if (tid < kD) shift[seq * shift_seq_stride + grp * kD + tid] = f2h(fs.osh[tid]);
   }
-  if (tid < kD) shift[seq * shift_seq_stride + grp * kD + tid] = f2h(fs.osh[tid]);
 }
 
 
@@ -503,6 +577,7 @@ __device__ __forceinline__ float fma_acc_f16(float z, uint32_t w, float acc) {
   return d;
 }
 
+template <bool DQ>
 __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma8_kernel(
     const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
     const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
@@ -634,14 +709,25 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma8_kernel(
 
   // <h, h_hat> = <z, h_hat> / s2 and ||h||^2 = d exactly (Normalize #2)
   const float alpha = (scale_adjust && dot > 0.f) ? (kD * s2) / dot : 1.0f;
-  if (hf == 0) {
+  if (hf == 0)
     *reinterpret_cast<u32x4*>(codes + seq * codes_seq_stride + tok * 16) =
         u32x4{cw[0], cw[1], cw[2], cw[3]};
-    const uint32_t mv = static_cast<uint32_t>(f2h(s1)) |
-                        (static_cast<uint32_t>(f2h(s2 * alpha)) << 16);
-    *reinterpret_cast<uint32_t*>(meta + seq * meta_seq_stride + 2 * tok) = mv;
+  if constexpr (DQ) {
+    __shared__ DqSmem dqs;
+    if (hf == 0) {
+      dqs.s1g[tok - grp * kG] = s1;
+      meta[seq * meta_seq_stride + tok] = f2h(s2 * alpha);
+    }
+    __syncthreads();
+    write_dq_record(fs.osh, dqs, reinterpret_cast<uint8_t*>(shift + seq * shift_seq_stride + grp * kDqRecU16));
+  } else {
+    if (hf == 0) {
+      const uint32_t mv = static_cast<uint32_t>(f2h(s1)) |
+                          (static_cast<uint32_t>(f2h(s2 * alpha)) << 16);
+      *reinterpret_cast<uint32_t*>(meta + seq * meta_seq_stride + 2 * tok) = mv;
+    }
+    if (tid < kD) shift[seq * shift_seq_stride + grp * kD + tid] = f2h(fs.osh[tid]);
   }
-  if (tid < kD) shift[seq * shift_seq_stride + grp * kD + tid] = f2h(fs.osh[tid]);
 }
 
 }  // namespace
@@ -653,8 +739,9 @@ bool quantize_mfma_supported(int in_f32, int sub_dim, int group_size) {
 hipError_t launch_quantize_mfma(const QuantArgs& a, hipStream_t s) {
   const int64_t n_groups = a.n_tok / kG;
   const int64_t blocks = a.n_seq * n_groups;
-  hipLaunchKernelGGL(a.sub_dim == 8 ? quantize_mfma8_kernel : quantize_mfma_kernel,
-                     dim3(static_cast<unsigned>(blocks)), dim3(kG * 2), 0, s,
+  auto kernel = a.sub_dim == 8 ? (a.dq ? quantize_mfma8_kernel<true> : quantize_mfma8_kernel<false>)
+                                : (a.dq ? quantize_mfma_kernel<true> : quantize_mfma_kernel<false>);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kG * 2), 0, s,
                      static_cast<const __half*>(a.x), n_groups, a.x_seq_stride,
                      static_cast<const uint8_t*>(a.table), a.codes, a.codes_seq_stride, a.meta,
                      a.meta_seq_stride, a.shift, a.shift_seq_stride, a.scale_adjust);

@@ -31,16 +31,12 @@ def ulp16(v):
     return np.spacing(v).astype(np.float64)
 
 
-def check_quantized_sequence(x, C, G, codes_g, meta_g, shift_g, scale_adjust=True):
-    """Compare one sequence's GPU output to the oracle.  Returns a dict of
-    statistics (number of accepted ties, ...).  Raises AssertionError."""
-    C64 = np.asarray(C, np.float64)
-    m = C64.shape[1]
-    codes_o, meta_o, shift_o, it = oracle.quantize(x, C, G, scale_adjust_on=scale_adjust,
-                                                   return_internals=True)
-    T = x.shape[0]
+def _check_codes(h_flat, C64, codes_g, codes_o):
+    """Codes equal to the oracle's except validated near-ties; returns their
+    number."""
+    T, m = h_flat.shape[0], C64.shape[1]
     assert codes_g.shape == codes_o.shape, (codes_g.shape, codes_o.shape)
-    h = it["h"].reshape(T, -1, m)
+    h = h_flat.reshape(T, -1, m)
     mism = np.argwhere(codes_g != codes_o)
     n_ties = 0
     for t, j in mism:
@@ -51,18 +47,95 @@ def check_quantized_sequence(x, C, G, codes_g, meta_g, shift_g, scale_adjust=Tru
             f"code mismatch at token {t}, sub-vector {j}: gpu {g} (D={dg:.9g}) vs oracle {o} "
             f"(D={do:.9g})")
         n_ties += 1
+    return n_ties
+
+
+def _check_s2(it, C64, codes_g, s2_g, scale_adjust):
+    """s2' within one fp16 ulp of the oracle's value for the GPU's codes."""
+    T = codes_g.shape[0]
+    hh = C64[codes_g.astype(np.int64)].reshape(T, -1)
+    alpha = oracle.scale_adjust(it["h"], hh) if scale_adjust else np.ones(T)
+    s2p = it["s2"] * alpha
+    s2_g = np.asarray(s2_g).astype(np.float64)
+    bad = np.abs(s2_g - s2p.astype(np.float16).astype(np.float64)) > ulp16(s2p) * 1.0001
+    assert not bad.any(), f"s2' off by more than 1 ulp at tokens {np.argwhere(bad)[:5].ravel()}"
+
+
+def _nibbles(b, n):
+    b = np.asarray(b, np.uint8)
+    out = np.empty(2 * b.size, np.int64)
+    out[0::2] = b & 15
+    out[1::2] = b >> 4
+    return out[:n]
+
+
+DQ_TIE = 1e-3   # distance of the oracle's fp32 grid coordinate from a half step
+
+
+def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128):
+    """Double-quantized output of one sequence against the oracle run on the
+    4-bit codebook C4: codes and s2' as in check_quantized_sequence; in each
+    group record lo, hi and the o' scale within one fp16 ulp; where they are
+    equal to the oracle's, the 4-bit codes equal its codes except near a half
+    step of the grid (differing by one); elsewhere the decoded values within
+    half a step of the exact ones.  Returns statistics."""
+    C64 = np.asarray(C4, np.float64)
+    codes_o, meta_o, shift_o, it = oracle.quantize(x, C4, G, scale_adjust_on=scale_adjust,
+                                                   return_internals=True)
+    n_ties = _check_codes(it["h"], C64, codes_g, codes_o)
+    _check_s2(it, C64, codes_g, s2_g, scale_adjust)
+    _, recs_o = oracle.dq_pack(meta_o, shift_o, it["s1"], it["o_rot"], G)
+    recs_g = np.asarray(recs_g, np.uint8).reshape(recs_o.shape)
+    d = 128
+    n_hdr = n_near = 0
+    for g in range(recs_o.shape[0]):
+        hg = recs_g[g, :6].view(np.float16).astype(np.float64)
+        ho = recs_o[g, :6].view(np.float16).astype(np.float64)
+        assert np.all(np.abs(hg - ho) <= ulp16(ho) * 1.0001), (g, hg, ho)
+        assert recs_g[g, 6] == 0 and recs_g[g, 7] == 0
+        s1x = it["s1"][g * G:(g + 1) * G]
+        ox = it["o_rot"][g]
+        if np.array_equal(recs_g[g, :8], recs_o[g, :8]):
+            lo, hi, sc = (np.float32(v) for v in ho)
+            for part, n, exact, ref in (("o", d, ox, None), ("s1", G, s1x, None)):
+                off = 8 if part == "o" else 8 + d // 2
+                cg = _nibbles(recs_g[g, off:off + n // 2], n)
+                co = _nibbles(recs_o[g, off:off + n // 2], n)
+                diff = np.argwhere(cg != co).ravel()
+                if diff.size == 0:
+                    continue
+                if part == "o":
+                    t = exact.astype(np.float32) / sc
+                else:
+                    t = (exact.astype(np.float32) - lo) * (np.float32(15) / (hi - lo))
+                t = t.astype(np.float64)
+                near = np.abs(t - np.floor(t) - 0.5) < DQ_TIE
+                assert np.all(near[diff]) and np.all(np.abs(cg[diff] - co[diff]) == 1), (
+                    f"group {g} {part} codes differ away from a half step at {diff[:5]}")
+                n_near += diff.size
+        else:
+            n_hdr += 1
+            s1d, od = oracle.dq_decode_group(recs_g[g], G, d)
+            lo, hi, sc = hg
+            assert np.abs(s1d - s1x).max() <= (hi - lo) / 30 * 1.001 + 2 * ulp16(hi)
+            assert np.abs(od - ox).max() <= sc / 2 * 1.001 + max(0.0, np.abs(ox).max() - 7 * sc) + 1e-7
+    return dict(ties=n_ties, codes=codes_o.size, near=n_near, hdr=n_hdr, groups=recs_o.shape[0])
+
+
+def check_quantized_sequence(x, C, G, codes_g, meta_g, shift_g, scale_adjust=True):
+    """Compare one sequence's GPU output to the oracle.  Returns a dict of
+    statistics (number of accepted ties, ...).  Raises AssertionError."""
+    C64 = np.asarray(C, np.float64)
+    m = C64.shape[1]
+    codes_o, meta_o, shift_o, it = oracle.quantize(x, C, G, scale_adjust_on=scale_adjust,
+                                                   return_internals=True)
+    n_ties = _check_codes(it["h"], C64, codes_g, codes_o)
     # s1
     s1_o = it["s1"]
     s1_g = meta_g[:, 0].astype(np.float64)
     bad = np.abs(s1_g - s1_o.astype(np.float16).astype(np.float64)) > ulp16(s1_o) * 1.0001
     assert not bad.any(), f"s1 off by more than 1 ulp at tokens {np.argwhere(bad)[:5].ravel()}"
-    # s2' with the GPU's codes
-    hh = C64[codes_g.astype(np.int64)].reshape(T, -1)
-    alpha = oracle.scale_adjust(it["h"], hh) if scale_adjust else np.ones(T)
-    s2p = it["s2"] * alpha
-    s2_g = meta_g[:, 1].astype(np.float64)
-    bad = np.abs(s2_g - s2p.astype(np.float16).astype(np.float64)) > ulp16(s2p) * 1.0001
-    assert not bad.any(), f"s2' off by more than 1 ulp at tokens {np.argwhere(bad)[:5].ravel()}"
+    _check_s2(it, C64, codes_g, meta_g[:, 1], scale_adjust)
     # rotated group mean
     sh_o = it["o_rot"]
     bad = np.abs(shift_g.astype(np.float64) - sh_o.astype(np.float16).astype(np.float64)) > \

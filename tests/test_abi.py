@@ -194,6 +194,32 @@ def test_attention_rope_validation(lib, q_pos, base, status):
     assert st == _lib.NSN_ERR_INVALID_ARG
 
 
+def test_double_quantization_validation(lib):
+    DQ = _lib.NSN_SCALE_ADJUST | _lib.NSN_DQ
+    # groups of 128 only, fp16 input only
+    assert _q(lib, P(G=256, flags=DQ), ms=256, ss=68) == _lib.NSN_ERR_UNSUPPORTED
+    assert _q(lib, P(flags=DQ), ms=256, ss=2 * 68, dtype=1) == _lib.NSN_ERR_UNSUPPORTED
+    # meta holds s2' alone and shift the 68-uint16 records: the strides follow
+    assert _q(lib, P(flags=DQ), ms=255, ss=2 * 68) == _lib.NSN_ERR_INVALID_ARG
+    assert _q(lib, P(flags=DQ), ms=256, ss=2 * 68 - 4) == _lib.NSN_ERR_INVALID_ARG
+    assert _q(lib, P(flags=DQ), ms=256, ss=2 * 68 + 2) == _lib.NSN_ERR_INVALID_ARG
+    assert _q(lib, P(flags=DQ), n_seq=0, ms=256, ss=2 * 68) == _lib.NSN_OK
+    f = lib.nsn_dequantize
+    assert f(P(flags=DQ), FAKE, 256 * 32, FAKE, 255, FAKE, 136, FAKE, 2, 256, 0, FAKE, 256 * 128,
+             NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(P(G=256, flags=DQ), FAKE, 256 * 32, FAKE, 256, FAKE, 136, FAKE, 2, 256, 0, FAKE,
+             256 * 128, NULL) == _lib.NSN_ERR_UNSUPPORTED
+    # rotary keys are not supported with it
+    s = _shape()
+    r = _lib.nsn_rope(10, 10000.0)
+    args = [FAKE] * 10
+    st = lib.nsn_decode_attention_rope(P(flags=DQ), ctypes.byref(s), ctypes.byref(r), *args, FAKE,
+                                       1 << 30, FAKE, NULL)
+    assert st == _lib.NSN_ERR_UNSUPPORTED
+    assert lib.nsn_decode_attention_workspace_size(P(flags=DQ), ctypes.byref(s)) > 0
+    assert lib.nsn_decode_attention_workspace_size(P(G=256, flags=DQ), ctypes.byref(s)) == 0
+
+
 def test_binding_inner_layout_checks():
     torch = pytest.importorskip("torch")
     import kv_cache_calibration_amd as nsnq

@@ -1,0 +1,262 @@
+"""Parity of the double-quantized path (NSN_DQ; NSNQuant summary, Methodology
+§3, Double Quantization) with the oracle: the prepared 4-bit codebook, the
+quantizer's codes, s2' and group records, dequantization and decode
+attention over the records, all through the C ABI."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import DEV, requires_gpu, torch
+from tests.golden import load_codebook
+from tests.parity import ATTN_ABS, SAME_BYTES_REL, check_dq_sequence, rel_l2
+
+import kv_cache_calibration_amd as nsnq
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+G = 128
+REC = oracle.record_bytes(G)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dq_table(m):
+    """(Params with NSN_DQ, device table, the oracle's 4-bit codebook)."""
+    C = load_codebook(m)
+    p = nsnq.Params(sub_dim=m, group_size=G, dq=True)
+    table = torch.empty(nsnq.nsn_table_size(p), dtype=torch.uint8, device=DEV)
+    nsnq.nsn_prepare_codebook(p, torch.from_numpy(C).to(DEV), table)
+    return p, table, oracle.codebook_4bit(C)
+
+
+def alloc_dq(n_seq, cap, m):
+    codes = torch.zeros((n_seq, cap, 128 // m), dtype=torch.uint8, device=DEV)
+    meta = torch.zeros((n_seq, cap), dtype=torch.float16, device=DEV)
+    recs = torch.zeros((n_seq, cap // G, REC), dtype=torch.uint8, device=DEV)
+    return codes, meta, recs
+
+
+def quantize_dq(x_np, m, pt=None):
+    p, table, C4 = pt or dq_table(m)
+    x = torch.from_numpy(np.ascontiguousarray(x_np)).to(DEV)
+    codes, meta, recs = alloc_dq(x.shape[0], x.shape[1], m)
+    nsnq.nsn_quantize(p, x, table, codes, meta, recs)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), meta.cpu().numpy(), recs.cpu().numpy(), (codes, meta, recs), (p, table, C4)
+
+
+@pytest.mark.parametrize("m", [4, 8])
+def test_prepared_codebook_is_the_4bit_codebook(m):
+    """The prepared table starts with the fp32 codebook the kernels search
+    (the table layout of the library's device header): bit-equal to the
+    oracle's nearest-level rounding, ties and zero included."""
+    C = load_codebook(m).copy()
+    C[0, 0], C[1, 0], C[2, 0], C[3, 0] = 0.375, -0.75, 0.0, 9.0     # ties, zero, beyond the range
+    p = nsnq.Params(sub_dim=m, group_size=G, dq=True)
+    table = torch.empty(nsnq.nsn_table_size(p), dtype=torch.uint8, device=DEV)
+    nsnq.nsn_prepare_codebook(p, torch.from_numpy(C).to(DEV), table)
+    got = table[:256 * m * 4].cpu().numpy().view(np.float32).reshape(256, m)
+    np.testing.assert_array_equal(got, oracle.codebook_4bit(C))
+
+
+@pytest.mark.parametrize("m,n_seq,T", [(4, 2, 512), (8, 2, 512), (4, 8, 4096), (8, 8, 4096)])
+def test_quantize_dq_parity(m, n_seq, T):
+    _say(f"quantize DQ m={m} n_seq={n_seq} T={T}")
+    K, V = synth.kv_numpy(n_seq // 2, T, 5.0, seed=1001, dtype=np.float16)
+    x = np.concatenate([K, V])
+    codes, meta, recs, _, (p, table, C4) = quantize_dq(x, m)
+    ties = near = hdr = total = 0
+    for s in range(x.shape[0]):
+        st = check_dq_sequence(x[s].astype(np.float64), C4, codes[s], meta[s], recs[s])
+        ties += st["ties"]
+        near += st["near"]
+        hdr += st["hdr"]
+        total += st["codes"]
+    assert ties <= max(2, total * 1e-4), (ties, total)
+    assert hdr <= max(1, x.shape[0] * T // G // 50), hdr
+    _say(f"  {ties} code near-ties of {total}, {near} record near-ties, {hdr} headers off by an ulp")
+
+
+def test_quantize_dq_strided_into_cache():
+    """Two sequences, three groups each, written at a group offset inside
+    larger caches; nothing outside the written slots changes."""
+    m = 4
+    K, _ = synth.kv_numpy(2, 3 * G, 5.0, seed=5, dtype=np.float16)
+    p, table, C4 = dq_table(m)
+    cap, off = 9 * G, 4 * G
+    codes, meta, recs = alloc_dq(2, cap, m)
+    x = torch.from_numpy(K).to(DEV)
+    nsnq.nsn_quantize(p, x, table, codes[:, off:], meta[:, off:], recs[:, off // G:])
+    torch.cuda.synchronize()
+    c, mt, rc = codes.cpu().numpy(), meta.cpu().numpy(), recs.cpu().numpy()
+    assert not c[:, :off].any() and not c[:, off + 3 * G:].any()
+    assert not mt[:, :off].any() and not mt[:, off + 3 * G:].any()
+    assert not rc[:, :off // G].any() and not rc[:, off // G + 3:].any()
+    for s in range(2):
+        check_dq_sequence(K[s].astype(np.float64), C4, c[s, off:off + 3 * G], mt[s, off:off + 3 * G],
+                          rc[s, off // G:off // G + 3])
+
+
+def test_quantize_dq_degenerate_groups():
+    """All-zero group (s1 and o' all 0: both scales 0, all codes 0) and a
+    constant group (hi == lo: s1 codes 0)."""
+    m = 4
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 3 * G, 128)).astype(np.float16)
+    x[0, :G] = 0
+    x[0, G:2 * G] = x[0, G]
+    codes, meta, recs, _, (p, table, C4) = quantize_dq(x, m)
+    assert not recs[0, 0].any()
+    lo, hi = recs[0, 1, :4].view(np.float16)
+    assert lo == hi and not recs[0, 1, 72:].any()
+    s1d, od = oracle.dq_decode_group(recs[0, 1], G)
+    want = np.linalg.norm(x[0, G].astype(np.float64)) / math.sqrt(128)
+    assert abs(s1d[0] - want) <= 1e-3 * want
+    check_dq_sequence(x[0, 2 * G:].astype(np.float64), C4, codes[0, 2 * G:], meta[0, 2 * G:],
+                      recs[0, 2:])
+
+
+@pytest.mark.parametrize("m,dt", [(4, torch.float32), (8, torch.float32), (4, torch.float16)])
+def test_dequantize_dq_parity(m, dt):
+    """GPU dequantization of the GPU's bytes against the oracle's
+    dequantization of the decoded records (1e-5 relative L2 for fp32
+    output, fp16 rounding otherwise); against the float64 input, the
+    reconstruction error stays within 1.2 times that of the plain fp16
+    metadata and the unrounded codebook (the oracle's: 1.16 times at most
+    on these inputs, for the keys with outlier channels at m = 4)."""
+    _say(f"dequantize DQ m={m} {dt}")
+    K, V = synth.kv_numpy(2, 1024, 5.0, seed=9, dtype=np.float16)
+    x = np.concatenate([K, V])
+    codes, meta, recs, (cd, md, rd), (p, table, C4) = quantize_dq(x, m)
+    out = torch.empty((4, 1024, 128), dtype=dt, device=DEV)
+    nsnq.nsn_dequantize(p, cd, md, rd, table, out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    tol = SAME_BYTES_REL if dt == torch.float32 else 1e-3
+    for s in range(4):
+        mt, sh = oracle.dq_unpack(meta[s], recs[s], G)
+        want = oracle.dequantize(codes[s], mt, sh, C4, G)
+        assert rel_l2(got[s], want) <= tol
+        xs = x[s].astype(np.float64)
+        C = load_codebook(m)
+        base = rel_l2(oracle.dequantize(*oracle.quantize(xs, C, G)[:3], C, G), xs)
+        assert rel_l2(want, xs) <= 1.2 * base
+
+
+def build_dq_cache(B, Hkv, Nq, R, m, seed, cap=None, rcap=None):
+    cap = cap or max(Nq, G)
+    rcap = rcap or max(R, 1)
+    p, table, C4 = dq_table(m)
+    n_seq = B * Hkv
+    Kn, Vn = synth.kv_numpy(n_seq, Nq + R, 5.0, seed=seed)
+    K, V = torch.from_numpy(Kn).to(DEV), torch.from_numpy(Vn).to(DEV)
+    kc, km, ks = alloc_dq(n_seq, cap, m)
+    vc, vm, vs = alloc_dq(n_seq, cap, m)
+    if Nq:
+        nsnq.nsn_quantize(p, K[:, :Nq], table, kc, km, ks)
+        nsnq.nsn_quantize(p, V[:, :Nq], table, vc, vm, vs)
+    kr = torch.zeros((n_seq, rcap, 128), dtype=torch.float16, device=DEV)
+    vr = torch.zeros_like(kr)
+    kr[:, :R] = K[:, Nq:]
+    vr[:, :R] = V[:, Nq:]
+
+    def v4(t):
+        return t.view(B, Hkv, *t.shape[1:])
+    return dict(p=p, table=table, C4=C4, k=(v4(kc), v4(km), v4(ks)), v=(v4(vc), v4(vm), v4(vs)),
+                kr=v4(kr), vr=v4(vr), Nq=Nq, R=R, B=B, Hkv=Hkv)
+
+
+def _decoded(cache_part, B, Hkv):
+    """Host (codes, meta float64 (s1, s2'), shift float64) from the records."""
+    c, mt, rc = (t.cpu().numpy() for t in cache_part)
+    cap = c.shape[2]
+    meta = np.zeros((B, Hkv, cap, 2))
+    shift = np.zeros((B, Hkv, cap // G, 128))
+    for b in range(B):
+        for h in range(Hkv):
+            meta[b, h], shift[b, h] = oracle.dq_unpack(mt[b, h], rc[b, h], G)
+    return c, meta, shift
+
+
+def run_dq_attention(cache, q, scale):
+    B, Hq, _ = q.shape
+    p = cache["p"]
+    ws = nsnq.nsn_decode_attention_workspace_size(p, B, Hq, cache["Hkv"], cache["Nq"], cache["R"],
+                                                  cache["k"][0].shape[2], cache["kr"].shape[2], scale)
+    work = torch.empty(max(ws, 16), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    nsnq.nsn_decode_attention(p, q, cache["k"], cache["v"], cache["kr"], cache["vr"], cache["table"],
+                              work, out, cache["Nq"], cache["R"], scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,R,m", [
+    (2, 8, 2, 1024, 16, 4),       # GQA 4:1
+    (1, 16, 2, 3072, 5, 4),       # two head blocks, ragged residual
+    (1, 8, 2, 2048, 64, 8),       # 1-bit codes
+    (1, 4, 1, 10240, 7, 4),       # several chunks, ragged chunk end
+    (1, 3, 1, 128, 200, 8),       # one group, three heads, long residual
+    (1, 4, 1, 0, 9, 4),           # residual only
+])
+def test_attention_dq_parity(B, Hq, Hkv, Nq, R, m):
+    _say(f"attention DQ B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} R={R} m={m}")
+    cache = build_dq_cache(B, Hkv, Nq, R, m, seed=51)
+    q = synth.query_torch((B, Hq, 128), seed=52, device=DEV)
+    scale = 1.0 / math.sqrt(128)
+    got = run_dq_attention(cache, q, scale)
+    k = _decoded(cache["k"], B, Hkv)
+    v = _decoded(cache["v"], B, Hkv)
+    want = oracle.decode_attention(q.cpu().numpy(), k, v, cache["kr"].cpu().numpy(),
+                                   cache["vr"].cpu().numpy(), cache["C4"], G, Nq, R, scale)
+    err = np.abs(got - want).max()
+    assert err <= ATTN_ABS, err
+    assert rel_l2(got, want) < 2e-3
+
+
+def test_attention_dq_decode_workload_sampled():
+    """The decode workload's shape (B=16, 32 q heads on 8 kv heads, 32768
+    quantized + 128 fp16 residual tokens) with double-quantized metadata;
+    sampled (batch, head) pairs against the oracle on the decoded records."""
+    w = synth.WORKLOADS["decode"]
+    _say("attention DQ decode workload (full size, sampled heads)")
+    B, Hq, Hkv, Nq, R = w["B"], w["Hq"], w["Hkv"], w["Nq"], w["R"]
+    p, table, C4 = dq_table(4)
+    n_seq = B * Hkv
+    K, V = synth.kv_torch(n_seq, Nq + R, 5.0, w["seed"], DEV)
+    kc, km, ks = alloc_dq(n_seq, Nq, 4)
+    vc, vm, vs = alloc_dq(n_seq, Nq, 4)
+    nsnq.nsn_quantize(p, K[:, :Nq], table, kc, km, ks)
+    nsnq.nsn_quantize(p, V[:, :Nq], table, vc, vm, vs)
+    kr = K[:, Nq:].contiguous()
+    vr = V[:, Nq:].contiguous()
+    del K, V
+
+    def v4(t):
+        return t.view(B, Hkv, *t.shape[1:])
+    cache = dict(p=p, table=table, k=(v4(kc), v4(km), v4(ks)), v=(v4(vc), v4(vm), v4(vs)),
+                 kr=v4(kr), vr=v4(vr), Nq=Nq, R=R, Hkv=Hkv)
+    q = synth.query_torch((B, Hq, 128), seed=w["seed"] + 1, device=DEV)
+    scale = 1.0 / math.sqrt(128)
+    got = run_dq_attention(cache, q, scale)
+    assert np.isfinite(got).all()
+    qn = q.cpu().numpy()
+    grp = Hq // Hkv
+    for b, h in [(0, 0), (5, 17), (B - 1, Hq - 1)]:
+        kvh = h // grp
+        sel = lambda part: tuple(t[b:b + 1, kvh:kvh + 1] for t in part)  # noqa: E731
+        k = _decoded(sel(cache["k"]), 1, 1)
+        v = _decoded(sel(cache["v"]), 1, 1)
+        want = oracle.decode_attention(qn[b:b + 1, h:h + 1], k, v,
+                                       cache["kr"][b:b + 1, kvh:kvh + 1].cpu().numpy(),
+                                       cache["vr"][b:b + 1, kvh:kvh + 1].cpu().numpy(), C4, G, Nq, R,
+                                       scale)
+        assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
