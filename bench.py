@@ -40,12 +40,27 @@ QUANT_SRC = os.path.join(ROOT, "kv_cache_calibration_amd", "csrc", "quantize_mfm
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_mfma_prefill_hbm_bytes.txt")
 
 
+DQ_REC = 136   # bytes of a double-quantized group record (G = 128)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def quant_bytes(n_seq, n_tok, m, G, in_bytes=2):
     return n_seq * n_tok * (D * in_bytes + D // m + 4) + n_seq * (n_tok // G) * D * 2
+
+
+def quant_bytes_dq(n_seq, n_tok, m, G, in_bytes=2):
+    """Double-quantized layout: s2' alone per token, one 136-byte record per group."""
+    return n_seq * n_tok * (D * in_bytes + D // m + 2) + n_seq * (n_tok // G) * DQ_REC
+
+
+def attn_bytes_dq(B, Hq, Hkv, Nq, R, m, G):
+    per_tok = 2 * (D // m) + 2 * 2                 # K and V codes + s2'
+    recs = 2 * (Nq // G) * DQ_REC                  # K and V group records
+    resid = 2 * R * D * 2
+    return B * Hkv * (Nq * per_tok + recs + resid) + B * Hq * D * (2 + 4)
 
 
 def attn_bytes(B, Hq, Hkv, Nq, R, m, G):
@@ -268,6 +283,51 @@ def main():
     ms_q1 = float(np.mean([a.elapsed_time(b) for a, b in evq1]))
     del codes1
 
+    # side measurements, outside the step: double-quantized metadata (4-bit
+    # s1 and rotated shift in one record per group, 4-bit codebook entries),
+    # the prefill quantize (its codes overwrite the step's) and the decode
+    # attention, same shapes
+    pq = nsnq.Params(sub_dim=m, group_size=G, dq=True)
+    tableq = torch.empty(nsnq.nsn_table_size(pq), dtype=torch.uint8, device=dev)
+    nsnq.nsn_prepare_codebook(pq, cb, tableq)
+    meta_q = torch.empty((n_seq, cap), dtype=torch.float16, device=dev)
+    recs_q = torch.empty((n_seq, cap // G, DQ_REC), dtype=torch.uint8, device=dev)
+    evqd = []
+    for i in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nsnq.nsn_quantize(pq, x, tableq, codes, meta_q, recs_q)
+        b.record(stream)
+        if i > 0:
+            evqd.append((a, b))
+    torch.cuda.synchronize()
+    ms_qdq = float(np.mean([a.elapsed_time(b) for a, b in evqd]))
+    del meta_q, recs_q
+    cachesq = []
+    for c in range(3):
+        K3, V3 = synth.kv_torch(B3 * Hkv, Nq + R, w3["outlier_scale"], w3["seed"] + 10 * c, dev)
+        kc = torch.empty((B3, Hkv, Nq, D // m), dtype=torch.uint8, device=dev)
+        km = torch.empty((B3, Hkv, Nq), dtype=torch.float16, device=dev)
+        ks = torch.empty((B3, Hkv, Nq // G, DQ_REC), dtype=torch.uint8, device=dev)
+        vc, vm, vs = torch.empty_like(kc), torch.empty_like(km), torch.empty_like(ks)
+        f = lambda t: t.view(B3 * Hkv, *t.shape[2:])  # noqa: E731
+        nsnq.nsn_quantize(pq, K3[:, :Nq], tableq, f(kc), f(km), f(ks))
+        nsnq.nsn_quantize(pq, V3[:, :Nq], tableq, f(vc), f(vm), f(vs))
+        cachesq.append(((kc, km, ks), (vc, vm, vs), caches[c][2], caches[c][3], caches[c][4]))
+        del K3, V3
+    evad = []
+    for i in range(max(args.steps, 3) + 1):
+        kcq, vcq, krq, vrq, qq = cachesq[i % 3]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nsnq.nsn_decode_attention(pq, qq, kcq, vcq, krq, vrq, tableq, work, out, Nq, R, scale)
+        b.record(stream)
+        if i > 0:
+            evad.append((a, b))
+    torch.cuda.synchronize()
+    ms_attn_dq = float(np.mean([a.elapsed_time(b) for a, b in evad]))
+    del cachesq
+
     qb = quant_bytes(n_seq, T, m, G)
     ab = attn_bytes(B3, Hq, Hkv, Nq, R, m, G)
     app_b = G * n_seq * D * 2 * 2
@@ -287,6 +347,10 @@ def main():
         "attention_rope_ms": ms_attn_rope,
         "quantize_1bit_gbps": quant_bytes(n_seq, T, m1, G) / (ms_q1 * 1e-3) / 1e9,
         "quantize_1bit_ms": ms_q1,
+        "quantize_dq_gbps": quant_bytes_dq(n_seq, T, m, G) / (ms_qdq * 1e-3) / 1e9,
+        "quantize_dq_ms": ms_qdq,
+        "attention_dq_gbps": attn_bytes_dq(B3, Hq, Hkv, Nq, R, m, G) / (ms_attn_dq * 1e-3) / 1e9,
+        "attention_dq_ms": ms_attn_dq,
         "flush_gbps": fb / (ms["flush"] * 1e-3) / 1e9,
         "dequantize_gbps": db / (ms["dequantize"] * 1e-3) / 1e9,
     }
@@ -295,6 +359,8 @@ def main():
     rates["attention_1bit_frac_hbm"] = rates["attention_1bit_gbps"] / HBM_PEAK_GBPS
     rates["quantize_1bit_frac_hbm"] = rates["quantize_1bit_gbps"] / HBM_PEAK_GBPS
     rates["attention_rope_frac_hbm"] = rates["attention_rope_gbps"] / HBM_PEAK_GBPS
+    rates["quantize_dq_frac_hbm"] = rates["quantize_dq_gbps"] / HBM_PEAK_GBPS
+    rates["attention_dq_frac_hbm"] = rates["attention_dq_gbps"] / HBM_PEAK_GBPS
     log("kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ms.items()))
     log("rates: " + ", ".join(f"{k} {v:.4g}" for k, v in rates.items()))
 
