@@ -41,6 +41,7 @@ from .nsn import (  # noqa: F401
     sq_dist_exact,
 )
 from .codebook import kmeans_codebook, round_to_fp16  # noqa: F401
+from .tune import cosine_loss, cosine_tune  # noqa: F401
 from .attention import (  # noqa: F401
     apply_rope,
     attend,
