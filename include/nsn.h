@@ -124,6 +124,42 @@ nsn_status nsn_build_codebook(int32_t sub_dim, int32_t n_codes,
                               void* stream);
 
 /*
+ * nsn_tune_codebook -- fine-tune a codebook for cosine distance.
+ * [NSNQuant summary §3, codebook construction: the k-means codebook is
+ *  fine-tuned to minimize the cosine distance between the original and
+ *  the quantized vectors, with no model involved; README, Codebook tuning.]
+ *
+ * The pages give the objective only; this call reads it as follows.
+ * vectors   device, float64 [n_vec][128]: training vectors (the NSN +
+ *           Hadamard output is standard normal, so N(0,1) draws; the
+ *           caller's generator).  Each is split into 128/sub_dim contiguous
+ *           sub-vectors, as the quantizer splits a token.
+ * codebook  device, float32 [n_codes][sub_dim]: the start (e.g. the output
+ *           of nsn_build_codebook) on entry, the tuned codebook on return,
+ *           rounded to the nearest fp16 value (ties to even).
+ * Each of `iters` iterations: assign every sub-vector its nearest codeword
+ * (exact squared distance in float64, lowest index on ties); with that
+ * assignment held fixed, take the gradient of the mean over vectors of
+ * 1 - cos(h, h_hat), h_hat the concatenated codewords; one Adam step on the
+ * whole batch (beta1 = 0.9, beta2 = 0.999, eps = 1e-8, bias-corrected
+ * moments starting at zero, learning rate lr).  Float64, sums in a fixed
+ * order: deterministic and reproducible bit for bit.  iters = 0 only
+ * rounds.  The README's 2-bit "--abs" option is not described on the pages
+ * and is not provided.
+ * Requires sub_dim in {4, 8}, n_codes == 256 (else NSN_ERR_UNSUPPORTED),
+ * 1 <= n_vec with n_vec*128/sub_dim <= 2^26, 0 <= iters <= 100000,
+ * 0 < lr <= 1, 16-byte aligned non-NULL pointers (else
+ * NSN_ERR_INVALID_ARG), workspace >= nsn_tune_codebook_workspace_size()
+ * (else NSN_ERR_WORKSPACE; the size query returns 0 for invalid shapes).
+ */
+size_t nsn_tune_codebook_workspace_size(int32_t sub_dim, int32_t n_codes,
+                                        int64_t n_vec);
+nsn_status nsn_tune_codebook(int32_t sub_dim, int32_t n_codes, int64_t n_vec,
+                             int32_t iters, double lr, const double* vectors,
+                             float* codebook, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * nsn_prepare_codebook -- derive the device search tables from a codebook.
  * codebook  device, float32 [256][sub_dim] (entries must be finite).
  * table     device, nsn_table_size(p) bytes, written; passed to every

@@ -28,6 +28,8 @@ __all__ = [
     "NsnError",
     "nsn_table_size",
     "nsn_build_codebook",
+    "nsn_tune_codebook",
+    "nsn_tune_codebook_workspace_size",
     "nsn_prepare_codebook",
     "nsn_nearest_codeword",
     "nsn_quantize",
@@ -114,6 +116,25 @@ def nsn_build_codebook(samples, codebook, workspace, iters=20, n_codes=256, stre
                                       _ptr(samples), _ptr(codebook), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+
+
+def nsn_tune_codebook(vectors, codebook, workspace, iters, lr=1e-3, n_codes=256, stream=None):
+    """vectors float64 (n_vec, 128) device; codebook float32 (n_codes, m) device,
+    the start on entry and the tuned, fp16-rounded codebook on return."""
+    import torch
+    _dev(vectors, codebook, workspace)
+    if vectors.dtype != torch.float64 or codebook.dtype != torch.float32:
+        raise ValueError("vectors must be float64 and codebook float32")
+    if not vectors.is_contiguous() or not codebook.is_contiguous() or vectors.shape[1] != 128:
+        raise ValueError("vectors (n, 128) and codebook must be contiguous")
+    lib = _lib.load()
+    _lib.check(lib.nsn_tune_codebook(codebook.shape[1], n_codes, vectors.shape[0], iters, lr,
+                                     _ptr(vectors), _ptr(codebook), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def nsn_tune_codebook_workspace_size(sub_dim, n_vec, n_codes=256):
+    return int(_lib.load().nsn_tune_codebook_workspace_size(sub_dim, n_codes, n_vec))
 
 
 def nsn_build_codebook_workspace_size(sub_dim, n_samples, n_codes=256):

@@ -62,6 +62,8 @@ SIGNATURES = {
     "nsn_table_size": (_SZ, [ctypes.POINTER(nsn_params)]),
     "nsn_build_codebook_workspace_size": (_SZ, [_I32, _I32, _I64]),
     "nsn_build_codebook": (_ST, [_I32, _I32, _I64, _I32, _P, _P, _P, _SZ, _P]),
+    "nsn_tune_codebook_workspace_size": (_SZ, [_I32, _I32, _I64]),
+    "nsn_tune_codebook": (_ST, [_I32, _I32, _I64, _I32, ctypes.c_double, _P, _P, _P, _SZ, _P]),
     "nsn_prepare_codebook": (_ST, [ctypes.POINTER(nsn_params), _P, _P, _SZ, _P]),
     "nsn_nearest_codeword": (_ST, [ctypes.POINTER(nsn_params), _P, _P, _I64, _P, _P]),
     "nsn_quantize": (_ST, [ctypes.POINTER(nsn_params), _ST, _P, _I64, _I64, _I64, _P,

@@ -131,6 +131,145 @@ __global__ void prepare_kernel(const float* __restrict__ cb, int dq, uint8_t* __
   tn[k] = n2;
 }
 
+// ---- fine-tuning on cosine distance
+// [NSNQuant summary, Methodology §3, codebook construction: the k-means
+//  codebook is fine-tuned to minimize the cosine distance between original
+//  and quantized vectors, without any model.]
+// Full d-dimensional vectors (d = 128) are split into d/m sub-vectors, each
+// assigned its nearest codeword (kmeans_assign on the same memory viewed as
+// sub-vectors).  Loss: mean over vectors of 1 - cos(h, h_hat).  With the
+// assignment held fixed, dL/dc_k = -(1/n) sum over the sub-vectors (i, j)
+// assigned to k of w_i (h_ij - r_i c_k), w_i = 1/sqrt(|h_i|^2 |h_hat_i|^2),
+// r_i = <h_i, h_hat_i>/|h_hat_i|^2 (both 0 when a norm is 0).  One
+// full-batch Adam step per iteration (Kingma and Ba, bias-corrected
+// moments).  Float64 without contraction, every sum left to right in a
+// fixed order: coordinates in index order, gradient terms in sample order.
+
+// Per vector: (w_i, r_i).
+template <int M>
+__global__ __launch_bounds__(256) void tune_stats(const double* __restrict__ h, int64_t n_vec,
+                                                  const int32_t* __restrict__ labels,
+                                                  const double* __restrict__ cent,
+                                                  double* __restrict__ wr) {
+#pragma clang fp contract(off)
+  constexpr int NS = kD / M;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n_vec) return;
+  double p = 0.0, a = 0.0, b = 0.0;
+  for (int j = 0; j < NS; ++j) {
+    const int k = labels[i * NS + j];
+#pragma unroll
+    for (int e = 0; e < M; ++e) {
+      const double x = h[i * kD + j * M + e], c = cent[k * M + e];
+      p = p + x * c;
+      a = a + x * x;
+      b = b + c * c;
+    }
+  }
+  const double ab = a * b;
+  double w = 0.0, r = 0.0;
+  if (ab > 0.0) {
+    w = 1.0 / sqrt(ab);
+    r = p / b;
+  }
+  wr[2 * i] = w;
+  wr[2 * i + 1] = r;
+}
+
+// Gradient of coordinate (k, e), summed over the members of k in sample
+// order, and the Adam update of that coordinate (it reads only its own
+// codeword, so the update is in place).
+struct AdamArgs {
+  double lr, b1, b2, eps, b1t, b2t;   // b1t, b2t = beta^t of this step
+};
+template <int M>
+__global__ __launch_bounds__(256) void tune_update(const double* __restrict__ h, int64_t n_vec,
+                                                   const int32_t* __restrict__ labels,
+                                                   const double* __restrict__ wr,
+                                                   double* __restrict__ cent, double* __restrict__ mom,
+                                                   double* __restrict__ vel, AdamArgs ad) {
+#pragma clang fp contract(off)
+  constexpr int NS = kD / M;
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id >= kCodes * M) return;
+  const int k = id / M, e = id % M;
+  const double c = cent[id];
+  const int64_t ns = n_vec * NS;
+  double s = 0.0;
+  for (int64_t i = 0; i < ns; ++i) {
+    if (labels[i] == k) {
+      const int64_t v = i / NS;
+      s = s + (h[i * M + e] - wr[2 * v + 1] * c) * wr[2 * v];
+    }
+  }
+  const double g = -s / static_cast<double>(n_vec);
+  const double mo = ad.b1 * mom[id] + (1.0 - ad.b1) * g;
+  const double ve = ad.b2 * vel[id] + (1.0 - ad.b2) * (g * g);
+  mom[id] = mo;
+  vel[id] = ve;
+  const double mhat = mo / (1.0 - ad.b1t);
+  const double vhat = ve / (1.0 - ad.b2t);
+  cent[id] = c - ad.lr * mhat / (sqrt(vhat) + ad.eps);
+}
+
+template <int M>
+__global__ void tune_init(const float* __restrict__ cb, double* __restrict__ cent,
+                          double* __restrict__ mom, double* __restrict__ vel) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id < kCodes * M) {
+    cent[id] = static_cast<double>(cb[id]);
+    mom[id] = 0.0;
+    vel[id] = 0.0;
+  }
+}
+
+struct TuneWs {
+  int32_t* labels;
+  double* wr;
+  double* cent;
+  double* mom;
+  double* vel;
+  size_t bytes;
+};
+TuneWs tune_ws(void* base, int sub_dim, int64_t n_vec) {
+  auto pad = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
+  const size_t lab = pad(static_cast<size_t>(n_vec) * (kD / sub_dim) * 4);
+  const size_t wr = pad(static_cast<size_t>(n_vec) * 2 * 8);
+  const size_t cb = pad(static_cast<size_t>(kCodes) * sub_dim * 8);
+  uint8_t* p = static_cast<uint8_t*>(base);
+  TuneWs w{};
+  w.labels = reinterpret_cast<int32_t*>(p);
+  w.wr = reinterpret_cast<double*>(p + lab);
+  w.cent = reinterpret_cast<double*>(p + lab + wr);
+  w.mom = reinterpret_cast<double*>(p + lab + wr + cb);
+  w.vel = reinterpret_cast<double*>(p + lab + wr + 2 * cb);
+  w.bytes = lab + wr + 3 * cb;
+  return w;
+}
+
+template <int M>
+hipError_t tune(int64_t n_vec, int iters, double lr, const double* vec, float* codebook, void* ws,
+                hipStream_t s) {
+  const TuneWs w = tune_ws(ws, M, n_vec);
+  const int cb_blocks = (kCodes * M + 255) / 256;
+  const int64_t ns = n_vec * (kD / M);
+  const unsigned ab = static_cast<unsigned>((ns + kAssignThreads - 1) / kAssignThreads);
+  const unsigned vb = static_cast<unsigned>((n_vec + 255) / 256);
+  hipLaunchKernelGGL(tune_init<M>, dim3(cb_blocks), dim3(256), 0, s, codebook, w.cent, w.mom, w.vel);
+  AdamArgs ad{lr, 0.9, 0.999, 1e-8, 1.0, 1.0};
+  for (int it = 0; it < iters; ++it) {
+    ad.b1t = ad.b1t * ad.b1;
+    ad.b2t = ad.b2t * ad.b2;
+    hipLaunchKernelGGL(kmeans_assign<M>, dim3(ab), dim3(kAssignThreads), 0, s, vec, ns, w.cent,
+                       w.labels);
+    hipLaunchKernelGGL(tune_stats<M>, dim3(vb), dim3(256), 0, s, vec, n_vec, w.labels, w.cent, w.wr);
+    hipLaunchKernelGGL(tune_update<M>, dim3(cb_blocks), dim3(256), 0, s, vec, n_vec, w.labels, w.wr,
+                       w.cent, w.mom, w.vel, ad);
+  }
+  hipLaunchKernelGGL(kmeans_finish<M>, dim3(cb_blocks), dim3(256), 0, s, w.cent, codebook);
+  return hipGetLastError();
+}
+
 template <int M>
 hipError_t build(int64_t n, int iters, const double* samples, float* codebook, void* ws,
                  hipStream_t s) {
@@ -163,6 +302,16 @@ hipError_t launch_build_codebook(int sub_dim, int n_codes, int64_t n, int iters,
   (void)n_codes;
   return sub_dim == 4 ? build<4>(n, iters, samples, codebook, ws, s)
                       : build<8>(n, iters, samples, codebook, ws, s);
+}
+
+size_t tune_codebook_workspace(int sub_dim, int64_t n_vec) {
+  return tune_ws(nullptr, sub_dim, n_vec).bytes;
+}
+
+hipError_t launch_tune_codebook(int sub_dim, int64_t n_vec, int iters, double lr,
+                                const double* vectors, float* codebook, void* ws, hipStream_t s) {
+  return sub_dim == 4 ? tune<4>(n_vec, iters, lr, vectors, codebook, ws, s)
+                      : tune<8>(n_vec, iters, lr, vectors, codebook, ws, s);
 }
 
 hipError_t launch_prepare_codebook(const float* codebook, int sub_dim, int dq, void* table,

@@ -109,6 +109,34 @@ nsn_status nsn_build_codebook(int32_t sub_dim, int32_t n_codes, int64_t n_sample
                     "nsn_build_codebook launch");
 }
 
+size_t nsn_tune_codebook_workspace_size(int32_t sub_dim, int32_t n_codes, int64_t n_vec) {
+  if ((sub_dim != 4 && sub_dim != 8) || n_codes != 256 || n_vec < 1) return 0;
+  return nsn::tune_codebook_workspace(sub_dim, n_vec);
+}
+
+nsn_status nsn_tune_codebook(int32_t sub_dim, int32_t n_codes, int64_t n_vec, int32_t iters,
+                             double lr, const double* vectors, float* codebook, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (sub_dim != 4 && sub_dim != 8)
+    return fail(NSN_ERR_UNSUPPORTED, "sub_dim must be 4 or 8 (got %d)", sub_dim);
+  if (n_codes != 256) return fail(NSN_ERR_UNSUPPORTED, "n_codes must be 256 (got %d)", n_codes);
+  if (n_vec < 1 || n_vec * (128 / sub_dim) > (int64_t(1) << 26))
+    return fail(NSN_ERR_INVALID_ARG, "n_vec must be in [1, 2^26 * sub_dim / 128] (got %lld)",
+                static_cast<long long>(n_vec));
+  if (iters < 0 || iters > 100000) return fail(NSN_ERR_INVALID_ARG, "iters must be in [0, 100000]");
+  if (!(lr > 0.0 && lr <= 1.0)) return fail(NSN_ERR_INVALID_ARG, "lr must be in (0, 1], got %g", lr);
+  if (!vectors || !codebook || !workspace)
+    return fail(NSN_ERR_INVALID_ARG, "vectors, codebook and workspace must be non-NULL");
+  if (!aligned16(vectors) || !aligned16(codebook) || !aligned16(workspace))
+    return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const size_t need = nsn::tune_codebook_workspace(sub_dim, n_vec);
+  if (workspace_bytes < need)
+    return fail(NSN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  return hip_status(nsn::launch_tune_codebook(sub_dim, n_vec, iters, lr, vectors, codebook, workspace,
+                                              static_cast<hipStream_t>(stream)),
+                    "nsn_tune_codebook launch");
+}
+
 nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook, void* table,
                                 size_t table_bytes, void* stream) {
   NSN_TRY(check_params(p));

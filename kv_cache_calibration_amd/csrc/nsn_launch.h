@@ -58,6 +58,10 @@ hipError_t launch_build_codebook(int sub_dim, int n_codes, int64_t n,
                                  float* codebook, void* workspace,
                                  hipStream_t s);
 size_t build_codebook_workspace(int sub_dim, int n_codes, int64_t n);
+hipError_t launch_tune_codebook(int sub_dim, int64_t n_vec, int iters, double lr,
+                                const double* vectors, float* codebook, void* workspace,
+                                hipStream_t s);
+size_t tune_codebook_workspace(int sub_dim, int64_t n_vec);
 
 hipError_t launch_residual_append(const uint16_t* tok, int64_t n_seq,
                                   uint16_t* resid, int64_t resid_seq_stride,

@@ -122,6 +122,24 @@ def test_build_codebook_validation(lib):
     assert f(4, 256, 65536, 20, FAKE, FAKE, FAKE, ws - 1, NULL) == _lib.NSN_ERR_WORKSPACE
 
 
+def test_tune_codebook_validation(lib):
+    f = lib.nsn_tune_codebook
+    ws = lib.nsn_tune_codebook_workspace_size(4, 256, 2048)
+    assert ws >= 2048 * 32 * 4 + 2048 * 16 + 3 * 256 * 4 * 8
+    assert lib.nsn_tune_codebook_workspace_size(3, 256, 2048) == 0
+    assert lib.nsn_tune_codebook_workspace_size(4, 256, 0) == 0
+    assert f(3, 256, 2048, 10, 1e-3, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_UNSUPPORTED
+    assert f(4, 512, 2048, 10, 1e-3, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_UNSUPPORTED
+    assert f(4, 256, 0, 10, 1e-3, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, (1 << 21) + 1, 10, 1e-3, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, 2048, -1, 1e-3, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    for lr in (0.0, -1e-3, 2.0, float("nan"), float("inf")):
+        assert f(4, 256, 2048, 10, lr, FAKE, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, 2048, 10, 1e-3, NULL, FAKE, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, 2048, 10, 1e-3, FAKE, MISALIGNED, FAKE, ws, NULL) == _lib.NSN_ERR_INVALID_ARG
+    assert f(4, 256, 2048, 10, 1e-3, FAKE, FAKE, FAKE, ws - 1, NULL) == _lib.NSN_ERR_WORKSPACE
+
+
 def test_prepare_and_append_validation(lib):
     ts = lib.nsn_table_size(P())
     assert ts >= 256 * 8 * 4
