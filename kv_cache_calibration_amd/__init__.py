@@ -69,7 +69,25 @@ class Params:
 
 def _stride16(t):
     """dim-0 stride in 2-byte units (meta and shift strides of the C ABI)."""
-    return t.stride(0) * t.element_size() // 2
+    b = t.stride(0) * t.element_size()
+    if b % 2:
+        raise ValueError("meta and shift sequence strides must be a whole number of 2-byte units")
+    return b // 2
+
+
+def _check_meta_layout(params, meta, shift):
+    """Inner shapes of meta and shift for the plain and the double-quantized
+    layouts (see the module doc)."""
+    if params.dq:
+        if meta.dim() != 2 or meta.element_size() != 2:
+            raise ValueError("with dq, meta is (n_seq, cap) of a 2-byte dtype (fp16 s2')")
+        if shift.dim() != 3 or shift.shape[2] * shift.element_size() != 136:
+            raise ValueError("with dq, shift is (n_seq, cap // 128, 136 bytes) of group records")
+    else:
+        if meta.dim() != 3 or meta.shape[2] != 2 or meta.element_size() != 2:
+            raise ValueError("meta is (n_seq, cap, 2) fp16")
+        if shift.dim() != 3 or shift.shape[2] != 128 or shift.element_size() != 2:
+            raise ValueError("shift is (n_seq, cap // G, 128) fp16")
 
 
 def _ptr(t):
@@ -183,6 +201,7 @@ def nsn_quantize(params, x, table, codes, meta, shift, n_tok=None, stream=None):
     _inner_contig(codes, None)
     _inner_contig(meta, None)
     _inner_contig(shift, None)
+    _check_meta_layout(params, meta, shift)
     lib = _lib.load()
     _lib.check(lib.nsn_quantize(ctypes.byref(params.c), _dtype_code(x), _ptr(x), x.shape[0], n_tok,
                                 x.stride(0), _ptr(table), _ptr(codes), codes.stride(0), _ptr(meta),
@@ -193,6 +212,10 @@ def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=No
     _dev(codes, meta, shift, table, out)
     n_tok = out.shape[1] if n_tok is None else n_tok
     _inner_contig(out, (out.shape[1], 128))
+    _inner_contig(codes, None)
+    _inner_contig(meta, None)
+    _inner_contig(shift, None)
+    _check_meta_layout(params, meta, shift)
     lib = _lib.load()
     _lib.check(lib.nsn_dequantize(ctypes.byref(params.c), _ptr(codes), codes.stride(0), _ptr(meta),
                                   _stride16(meta), _ptr(shift), _stride16(shift), _ptr(table),
@@ -247,6 +270,33 @@ def nsn_decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, w
                       n_quant_tok, n_resid_tok, softmax_scale, stream, None)
 
 
+def _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out):
+    """The sizes the C ABI derives from the shape struct must match the
+    tensors: q and out (B, Hq, 128), codes (B, Hkv, cap, 128 // m), meta
+    and shift per layout, residuals (B, Hkv, Rcap, 128)."""
+    B, Hq = q.shape[0], q.shape[1]
+    kc = k_cache[0]
+    Hkv, cap = kc.shape[1], kc.shape[2]
+    G = params.group_size
+    if tuple(q.shape) != (B, Hq, 128) or tuple(out.shape) != (B, Hq, 128):
+        raise ValueError("q and out must be (B, Hq, 128)")
+    for c, mt, sh in (k_cache, v_cache):
+        if tuple(c.shape) != (B, Hkv, cap, 128 // params.sub_dim):
+            raise ValueError("codes must be (B, Hkv, cap, 128 // m), alike for K and V")
+        if params.dq:
+            ok = (tuple(mt.shape) == (B, Hkv, cap) and mt.element_size() == 2 and
+                  tuple(sh.shape[:3]) == (B, Hkv, cap // G) and sh.dim() == 4 and
+                  sh.shape[3] * sh.element_size() == 136)
+        else:
+            ok = (tuple(mt.shape) == (B, Hkv, cap, 2) and mt.element_size() == 2 and
+                  tuple(sh.shape) == (B, Hkv, cap // G, 128) and sh.element_size() == 2)
+        if not ok:
+            raise ValueError("meta / shift shapes do not match the cache layout")
+    for r in (k_resid, v_resid):
+        if r.dim() != 4 or tuple(r.shape[:2]) != (B, Hkv) or r.shape[3] != 128 or r.shape != k_resid.shape:
+            raise ValueError("residuals must be (B, Hkv, Rcap, 128), alike for K and V")
+
+
 def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
                       n_quant_tok, n_resid_tok, softmax_scale, stream, rope):
     kc, km, ks = k_cache
@@ -257,6 +307,7 @@ def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, work
             raise ValueError("attention tensors must be contiguous")
     B, Hq, _ = q.shape
     Hkv, cap = kc.shape[1], kc.shape[2]
+    _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out)
     s = _shape(B, Hq, Hkv, n_quant_tok, n_resid_tok, cap, k_resid.shape[2], softmax_scale)
     lib = _lib.load()
     bufs = (_ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc), _ptr(vm), _ptr(vs), _ptr(k_resid),

@@ -120,7 +120,7 @@ nsn_status nsn_tune_codebook(int32_t sub_dim, int32_t n_codes, int64_t n_vec, in
   if (sub_dim != 4 && sub_dim != 8)
     return fail(NSN_ERR_UNSUPPORTED, "sub_dim must be 4 or 8 (got %d)", sub_dim);
   if (n_codes != 256) return fail(NSN_ERR_UNSUPPORTED, "n_codes must be 256 (got %d)", n_codes);
-  if (n_vec < 1 || n_vec * (128 / sub_dim) > (int64_t(1) << 26))
+  if (n_vec < 1 || n_vec > ((int64_t(1) << 26) / (128 / sub_dim)))
     return fail(NSN_ERR_INVALID_ARG, "n_vec must be in [1, 2^26 * sub_dim / 128] (got %lld)",
                 static_cast<long long>(n_vec));
   if (iters < 0 || iters > 100000) return fail(NSN_ERR_INVALID_ARG, "iters must be in [0, 100000]");

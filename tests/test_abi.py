@@ -253,3 +253,46 @@ def test_binding_inner_layout_checks():
         nsnq._dev(t)                              # host tensors are rejected
     p = nsnq.Params(sub_dim=8, group_size=256, scale_adjust=False)
     assert (p.c.sub_dim, p.c.group_size, p.c.flags, p.c.head_dim) == (8, 256, 0, 128)
+
+
+def test_binding_layout_checks_of_both_metadata_layouts():
+    """The binding checks meta / shift / cache shapes against the layout the
+    params select, before any call (host tensors suffice here)."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    p = nsnq.Params(sub_dim=4, group_size=128)
+    pd = nsnq.Params(sub_dim=4, group_size=128, dq=True)
+    assert pd.dq and not p.dq and pd.c.flags == _lib.NSN_SCALE_ADJUST | _lib.NSN_DQ
+    meta = torch.zeros((2, 256, 2), dtype=torch.float16)
+    shift = torch.zeros((2, 2, 128), dtype=torch.float16)
+    meta_dq = torch.zeros((2, 256), dtype=torch.float16)
+    recs = torch.zeros((2, 2, 136), dtype=torch.uint8)
+    nsnq._check_meta_layout(p, meta, shift)
+    nsnq._check_meta_layout(pd, meta_dq, recs)
+    nsnq._check_meta_layout(pd, meta_dq, recs.view(torch.int16))
+    for args in ((p, meta_dq, recs), (pd, meta, shift), (pd, meta_dq, recs[:, :, :135])):
+        with pytest.raises(ValueError):
+            nsnq._check_meta_layout(*args)
+    with pytest.raises(ValueError):
+        nsnq._stride16(torch.zeros((3, 135), dtype=torch.uint8))
+    assert nsnq._stride16(recs) == 136
+    # attention shapes
+    B, Hq, Hkv, cap, R = 2, 8, 2, 256, 16
+    q = torch.zeros((B, Hq, 128), dtype=torch.float16)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32)
+    kc = torch.zeros((B, Hkv, cap, 32), dtype=torch.uint8)
+    plain = (kc, torch.zeros((B, Hkv, cap, 2), dtype=torch.float16),
+             torch.zeros((B, Hkv, cap // 128, 128), dtype=torch.float16))
+    dq = (kc, torch.zeros((B, Hkv, cap), dtype=torch.float16),
+          torch.zeros((B, Hkv, cap // 128, 136), dtype=torch.uint8))
+    kr = torch.zeros((B, Hkv, R, 128), dtype=torch.float16)
+    nsnq._check_attention_shapes(p, q, plain, plain, kr, kr, out)
+    nsnq._check_attention_shapes(pd, q, dq, dq, kr, kr, out)
+    with pytest.raises(ValueError):
+        nsnq._check_attention_shapes(p, q, dq, dq, kr, kr, out)
+    with pytest.raises(ValueError):
+        nsnq._check_attention_shapes(pd, q, plain, plain, kr, kr, out)
+    with pytest.raises(ValueError):
+        nsnq._check_attention_shapes(p, q, plain, plain, kr, kr[:, :, :8], out)
+    with pytest.raises(ValueError):
+        nsnq._check_attention_shapes(nsnq.Params(sub_dim=8), q, plain, plain, kr, kr, out)
