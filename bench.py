@@ -488,7 +488,10 @@ def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = None
-    cores = len(os.sched_getaffinity(0))
+    # threads the oracle actually runs on: numpy's element-wise work is
+    # single-threaded, its matrix products use the BLAS pool
+    affinity = len(os.sched_getaffinity(0))
+    cores = blas_threads if blas_threads else 1
     # quantize sample: whole prefill sequences of 8192 tokens until ~10 s
     n_tok = 8192
     tq, n_q = 0.0, 0
@@ -519,6 +522,7 @@ def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
         "unit": "GB/s",
         "cores": cores,
         "blas_threads": blas_threads,
+        "host_cores_available": affinity,
         "kind": "oracle",
         "sample": (f"oracle.quantize on {n_q} prefill sequences x {n_tok} tokens ({tq:.1f} s) and "
                    f"oracle.decode_attention {n_a}x on one (batch, kv head) of the decode cache "
