@@ -146,3 +146,28 @@ def test_attention_decode_workload_sampled():
                                        cache["C"], w["G"], w["Nq"], w["R"], 1 / math.sqrt(128))
         err = np.abs(got[b, h] - want[0, 0]).max()
         assert err <= ATTN_ABS, (b, h, err)
+
+
+@pytest.mark.parametrize("m,G", [(4, 128), (8, 256)])
+def test_attention_largest_chunk_sampled(m, G):
+    """Enough (batch, kv head) rows that one workgroup takes the largest chunk
+    (8192 quantized tokens: 128 tiles, 64 groups of 128 in LDS), two chunks
+    per row; sampled heads vs the oracle on the same cache bytes."""
+    B, Hq, Hkv, Nq, R = 64, 32, 8, 16384, 3
+    print(f"attention largest chunk m={m} G={G}", flush=True)
+    cache = build_cache(B, Hkv, Nq, R, m, G, seed=71, device_gen=True)
+    scale = 1 / math.sqrt(128)
+    ws = nsnq.nsn_decode_attention_workspace_size(cache["p"], B, Hq, Hkv, Nq, R, Nq, R, scale)
+    assert ws == B * Hq * (2 + 1) * 132 * 4          # two chunks of 8192 + the residual partial
+    q = synth.query_torch((B, Hq, 128), seed=72, device=DEV)
+    got = run_gpu(cache, q, scale)
+    assert np.isfinite(got).all()
+    qn = q.cpu().numpy()
+    for b, h in [(0, 0), (17, 9), (B - 1, Hq - 1)]:
+        kvh = h // (Hq // Hkv)
+        sl = lambda t: t[b:b + 1, kvh:kvh + 1].cpu().numpy()  # noqa: E731
+        k = tuple(sl(t) for t in cache["k"])
+        v = tuple(sl(t) for t in cache["v"])
+        want = oracle.decode_attention(qn[b:b + 1, h:h + 1], k, v, sl(cache["kr"]), sl(cache["vr"]),
+                                       cache["C"], G, Nq, R, scale)
+        assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)

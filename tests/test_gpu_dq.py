@@ -260,3 +260,44 @@ def test_attention_dq_decode_workload_sampled():
                                        cache["vr"][b:b + 1, kvh:kvh + 1].cpu().numpy(), C4, G, Nq, R,
                                        scale)
         assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
+
+
+def test_attention_dq_largest_chunk_sampled():
+    """One workgroup per 8192-token chunk (64 group records decoded into LDS),
+    two chunks per (batch, kv head) row; sampled heads against the oracle on
+    the decoded records."""
+    B, Hq, Hkv, Nq, R = 64, 32, 8, 16384, 3
+    _say("attention DQ largest chunk")
+    p, table, C4 = dq_table(4)
+    n_seq = B * Hkv
+    K, V = synth.kv_torch(n_seq, Nq + R, 5.0, 81, DEV)
+    kc, km, ks = alloc_dq(n_seq, Nq, 4)
+    vc, vm, vs = alloc_dq(n_seq, Nq, 4)
+    nsnq.nsn_quantize(p, K[:, :Nq], table, kc, km, ks)
+    nsnq.nsn_quantize(p, V[:, :Nq], table, vc, vm, vs)
+    kr = K[:, Nq:].contiguous()
+    vr = V[:, Nq:].contiguous()
+    del K, V
+
+    def v4(t):
+        return t.view(B, Hkv, *t.shape[1:])
+    cache = dict(p=p, table=table, k=(v4(kc), v4(km), v4(ks)), v=(v4(vc), v4(vm), v4(vs)),
+                 kr=v4(kr), vr=v4(vr), Nq=Nq, R=R, Hkv=Hkv)
+    scale = 1.0 / math.sqrt(128)
+    ws = nsnq.nsn_decode_attention_workspace_size(p, B, Hq, Hkv, Nq, R, Nq, R, scale)
+    assert ws == B * Hq * (2 + 1) * 132 * 4
+    q = synth.query_torch((B, Hq, 128), seed=82, device=DEV)
+    got = run_dq_attention(cache, q, scale)
+    assert np.isfinite(got).all()
+    qn = q.cpu().numpy()
+    grp = Hq // Hkv
+    for b, h in [(0, 0), (33, 14), (B - 1, Hq - 1)]:
+        kvh = h // grp
+        sel = lambda part: tuple(t[b:b + 1, kvh:kvh + 1] for t in part)  # noqa: E731
+        k = _decoded(sel(cache["k"]), 1, 1)
+        v = _decoded(sel(cache["v"]), 1, 1)
+        want = oracle.decode_attention(qn[b:b + 1, h:h + 1], k, v,
+                                       cache["kr"][b:b + 1, kvh:kvh + 1].cpu().numpy(),
+                                       cache["vr"][b:b + 1, kvh:kvh + 1].cpu().numpy(), C4, G, Nq, R,
+                                       scale)
+        assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
