@@ -278,6 +278,22 @@ __device__ __forceinline__ v8h hblk(const HOps& o, int a, int kb) {
   return __builtin_bit_cast(v8h, (kb & 1) ? (neg ? o.N1 : o.P1) : (neg ? o.N0 : o.P0));
 }
 
+// fp16 pair (round to nearest even) of (z0, z1), each rounded once, and the
+// fp16 pair of the remainders (z0 - hi0, z1 - hi1): together about 22
+// significant bits.  Arithmetic only.
+__device__ __forceinline__ uint32_t f16_hi2(float z0, float z1) {
+  uint32_t h;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, 0 op_sel_hi:[0,0,0]" : "=v"(h) : "v"(z0));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, 0 op_sel_hi:[0,0,0]" : "+v"(h) : "v"(z1));
+  return h;
+}
+__device__ __forceinline__ uint32_t f16_lo2(float z0, float z1, uint32_t hi) {
+  uint32_t l;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[0,0,1]" : "=v"(l) : "v"(z0), "v"(hi));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(l) : "v"(z1), "v"(hi));
+  return l;
+}
+
 // Rotary angle: theta_i = base^(-i/64) for channel pair (i, i + 64).
 __device__ __forceinline__ double rope_theta(float base, int i) {
   return pow(static_cast<double>(base), -static_cast<double>(i) / 64.0);
@@ -752,6 +768,31 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       }
       rope_query(rsm, rsm.qp[wave], lane, theta, p.q_pos - (static_cast<int64_t>(c0) + tau * kTile));
       wave_lds_sync();
+      // The turned queries as the A operand of v_mfma_f32_32x32x16_f16 for
+      // the key dot products: row l % 32 = slot (0..3: fp16 high part of
+      // head 0..3, 4..7: low part, the rest 0); K slice s = 4pm + q holds
+      // channels 32pm + 8q + [0, 8) and those + 64, lane half hA supplying
+      // K = 8hA + v: v < 4 channel 32pm + 8q + 4hA + v, v >= 4 the same
+      // channel + 64 (the key operand below uses the same order).
+      u32x4 qk[8];
+      {
+        const int row = lane & 31, hA = lane >> 5;
+        const int hq = row & 3, part = row >> 2;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int c = 32 * (sl >> 2) + 8 * (sl & 3) + 4 * hA;
+          const float4 u = *reinterpret_cast<const float4*>(&rsm.qp[wave][hq][c]);
+          const float4 v = *reinterpret_cast<const float4*>(&rsm.qp[wave][hq][c + kD / 2]);
+          uint32_t w4[4] = {f16_hi2(u.x, u.y), f16_hi2(u.z, u.w), f16_hi2(v.x, v.y), f16_hi2(v.z, v.w)};
+          if (part == 1) {
+            w4[0] = f16_lo2(u.x, u.y, w4[0]);
+            w4[1] = f16_lo2(u.z, u.w, w4[1]);
+            w4[2] = f16_lo2(v.x, v.y, w4[2]);
+            w4[3] = f16_lo2(v.z, v.w, w4[3]);
+          }
+          qk[sl] = part < 2 ? u32x4{w4[0], w4[1], w4[2], w4[3]} : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
       // Two halves of 32 keys.  The MFMA token-major pass gives lane
       // (t32, hf) the channels {32mb + 8(r/4) + 4hf + r%4} of key 32ht + t32:
       // both members of every rotary pair (c, c + 64) sit in one lane.
@@ -787,14 +828,17 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
             xv[kb] = *reinterpret_cast<const u32x4*>(&sm.cbh[4 * ci]);
           }
         }
-        // k = s1 (s2' H c / sqrt(d) + og), turned by the key's offset, dotted
-        // with the turned queries over this lane's 64 channels (s1 applied to
-        // the sum); row blocks (pm, pm + 2) hold the pairs (c, c + 64) of
-        // channels 32pm ..
+        // k = s1 (s2' H c / sqrt(d) + og), turned by the key's offset (s1
+        // applied to the score); row blocks (pm, pm + 2) hold the pairs
+        // (c, c + 64) of channels 32pm ..  The turned key, split into fp16
+        // high and low parts, is the B operand (K = this lane's channels,
+        // N = its key) of the dot products with the queries: rows 0..3 of
+        // the result (lane half 0) and 4..7 (half 1) are the high and low
+        // query parts of heads 0..3.
         const uint32_t kmt = __shfl(d.km, tok, kWave);
         const float s1k = h2f(kmt & 0xffffu), s2k = h2f(kmt >> 16);
         const float a = s2k * kInvSqrtD;
-        float part[kHB] = {0.f, 0.f, 0.f, 0.f};
+        v16f dq = v16f{};
 #pragma unroll
         for (int pm = 0; pm < 2; ++pm) {
           v16f hx = v16f{}, hy = v16f{};
@@ -809,31 +853,30 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
             const float4 ox = *reinterpret_cast<const float4*>(&rsm.og[wave][cb0]);
             const float4 oy = *reinterpret_cast<const float4*>(&rsm.og[wave][cb0 + kD / 2]);
             const float oxv[4] = {ox.x, ox.y, ox.z, ox.w}, oyv[4] = {oy.x, oy.y, oy.z, oy.w};
-            float qx[kHB][4], qy[kHB][4];
-#pragma unroll
-            for (int h = 0; h < kHB; ++h) {
-              const float4 u = *reinterpret_cast<const float4*>(&rsm.qp[wave][h][cb0]);
-              const float4 v = *reinterpret_cast<const float4*>(&rsm.qp[wave][h][cb0 + kD / 2]);
-              qx[h][0] = u.x; qx[h][1] = u.y; qx[h][2] = u.z; qx[h][3] = u.w;
-              qy[h][0] = v.x; qy[h][1] = v.y; qy[h][2] = v.z; qy[h][3] = v.w;
-            }
+            float kx[4], ky[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g4 + e;
               const float2 cs = rsm.tab[cb0 + e][tok];
               const float x = fmaf(a, hx[r], oxv[e]);
               const float y = fmaf(a, hy[r], oyv[e]);
-              const float kx = x * cs.x - y * cs.y;
-              const float ky = y * cs.x + x * cs.y;
-#pragma unroll
-              for (int h = 0; h < kHB; ++h) part[h] = fmaf(qy[h][e], ky, fmaf(qx[h][e], kx, part[h]));
+              kx[e] = x * cs.x - y * cs.y;
+              ky[e] = y * cs.x + x * cs.y;
             }
+            const uint32_t h0 = f16_hi2(kx[0], kx[1]), h1 = f16_hi2(kx[2], kx[3]);
+            const uint32_t h2 = f16_hi2(ky[0], ky[1]), h3 = f16_hi2(ky[2], ky[3]);
+            const u32x4 bh = u32x4{h0, h1, h2, h3};
+            const u32x4 bl = u32x4{f16_lo2(kx[0], kx[1], h0), f16_lo2(kx[2], kx[3], h1),
+                                   f16_lo2(ky[0], ky[1], h2), f16_lo2(ky[2], ky[3], h3)};
+            const v8h qa = __builtin_bit_cast(v8h, qk[4 * pm + g4]);
+            dq = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, __builtin_bit_cast(v8h, bh), dq, 0, 0, 0);
+            dq = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, __builtin_bit_cast(v8h, bl), dq, 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int h = 0; h < kHB; ++h) {
-          const float v = half_pair_sum(part[h]) * s1k;
+          const float v = half_pair_sum(dq[h]) * s1k;
           sh[h] = ht == hf ? v : sh[h];
         }
         __builtin_amdgcn_sched_barrier(0);
