@@ -191,3 +191,57 @@ def test_residual_append_writes_the_slot():
     r = resid.cpu()
     assert torch.equal(r[:, 7], tok.cpu())
     assert not r[:, :7].any() and not r[:, 8:].any()
+
+
+def test_quantize_prefill_full_size_sampled():
+    """The prefill workload at full size in the launch the benchmark times:
+    2048 sequences (32 layers x batch 4 x 8 kv heads, K and V) x 131072 fp16
+    tokens in one nsn_quantize call, for 2-bit codes, 1-bit codes and the
+    double-quantized layout.  Groups are independent, so each sampled group of
+    128 tokens is checked against the oracle run on that group alone."""
+    from tests.gpu_common import table_for as _tf
+    from tests.parity import check_dq_sequence
+    w = synth.WORKLOADS["prefill"]
+    G, T, L = w["G"], w["T"], 32
+    per_layer = w["B"] * w["Hkv"]
+    n_seq_t = per_layer * L
+    n_seq = 2 * n_seq_t
+    _say(f"quantize prefill full size: {n_seq} sequences x {T} tokens")
+    x = torch.empty((n_seq, T, 128), dtype=torch.float16, device=DEV)
+    for layer in range(L):
+        a, b = layer * per_layer, (layer + 1) * per_layer
+        synth.kv_torch(per_layer, T, w["outlier_scale"], w["seed"] + layer, DEV,
+                       out_k=x[a:b], out_v=x[n_seq_t + a:n_seq_t + b])
+    rng = np.random.default_rng(2024)
+    picks = [(0, 0), (n_seq - 1, T // G - 1), (n_seq_t, 517)]
+    picks += [(int(s), int(g)) for s, g in zip(rng.integers(0, n_seq, 6), rng.integers(0, T // G, 6))]
+    xs = {pk: x[pk[0], pk[1] * G:(pk[1] + 1) * G].cpu().numpy().astype(np.float64) for pk in picks}
+    for m in (4, 8):
+        p, table, C = _tf(m, G)
+        codes = torch.empty((n_seq, T, 128 // m), dtype=torch.uint8, device=DEV)
+        meta = torch.empty((n_seq, T, 2), dtype=torch.float16, device=DEV)
+        shift = torch.empty((n_seq, T // G, 128), dtype=torch.float16, device=DEV)
+        nsnq.nsn_quantize(p, x, table, codes, meta, shift)
+        torch.cuda.synchronize()
+        _say(f"  m={m} quantized, checking {len(picks)} sampled groups")
+        for (s, g), xg in xs.items():
+            sl = slice(g * G, (g + 1) * G)
+            check_quantized_sequence(xg, C, G, codes[s, sl].cpu().numpy(), meta[s, sl].cpu().numpy(),
+                                     shift[s, g:g + 1].cpu().numpy())
+        del codes, meta, shift
+    # double-quantized metadata, 2-bit
+    C = table_for(4, G)[2]
+    pd = nsnq.Params(sub_dim=4, group_size=G, dq=True)
+    tabd = torch.empty(nsnq.nsn_table_size(pd), dtype=torch.uint8, device=DEV)
+    nsnq.nsn_prepare_codebook(pd, torch.from_numpy(C).to(DEV), tabd)
+    codes = torch.empty((n_seq, T, 32), dtype=torch.uint8, device=DEV)
+    meta = torch.empty((n_seq, T), dtype=torch.float16, device=DEV)
+    recs = torch.empty((n_seq, T // G, oracle.record_bytes(G)), dtype=torch.uint8, device=DEV)
+    nsnq.nsn_quantize(pd, x, tabd, codes, meta, recs)
+    torch.cuda.synchronize()
+    _say(f"  double-quantized layout quantized, checking {len(picks)} sampled groups")
+    C4 = oracle.codebook_4bit(C)
+    for (s, g), xg in xs.items():
+        sl = slice(g * G, (g + 1) * G)
+        check_dq_sequence(xg, C4, codes[s, sl].cpu().numpy(), meta[s, sl].cpu().numpy(),
+                          recs[s, g:g + 1].cpu().numpy())
