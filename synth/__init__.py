@@ -38,7 +38,11 @@ __all__ = [
 
 HEAD_DIM = 128
 
-# The five workloads (sizes only; see the design doc for the mapping).
+# The five workloads, sizes only: tiny (fp32, G = 256: the oracle finishes it
+# at once), one layer's K and V at 2 and at 1 bit, the decode-attention shape
+# (batch 16, 32 query heads on 8 kv heads, 32768 quantized + 128 fp16
+# residual tokens) and the full prefill (32 layers x batch 4 x 8 kv heads x
+# 131072 tokens, K and V).
 WORKLOADS = {
     "tiny": dict(n_seq=1, T=256, G=256, m=4, dtype="f32", outlier_scale=1.0,
                  cb_samples=65536, seed=1000),
