@@ -115,6 +115,7 @@ struct RopeSmem {
   float q[kHB][kD];              // the block's queries, original domain
   float qp[kWaves][kHB][kD];     // per wave: the queries turned by q_pos - P
   float og[kWaves][kD];          // per wave: the tile's group shift, original domain
+  u32x4 qkl[kWaves][8][2][8];   // per wave: the query MFMA operand, [slice][lane half][row]
 };
 struct NoRopeSmem {
   int unused;
@@ -770,14 +771,16 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       wave_lds_sync();
       // The turned queries as the A operand of v_mfma_f32_32x32x16_f16 for
       // the key dot products: row l % 32 = slot (0..3: fp16 high part of
-      // head 0..3, 4..7: low part, the rest 0); K slice s = 4pm + q holds
-      // channels 32pm + 8q + [0, 8) and those + 64, lane half hA supplying
-      // K = 8hA + v: v < 4 channel 32pm + 8q + 4hA + v, v >= 4 the same
-      // channel + 64 (the key operand below uses the same order).
-      u32x4 qk[8];
+      // head 0..3, 4..7: low part); K slice s = 4pm + q holds channels
+      // 32pm + 8q + [0, 8) and those + 64, lane half hA supplying K = 8hA + v:
+      // v < 4 channel 32pm + 8q + 4hA + v, v >= 4 the same channel + 64 (the
+      // key operand below uses the same order).  Kept in LDS (registers are
+      // the limit here); lanes of rows 8..31 read a copy of row l % 8, whose
+      // output rows are never used.
       {
         const int row = lane & 31, hA = lane >> 5;
         const int hq = row & 3, part = row >> 2;
+        if (row < 8)
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
           const int c = 32 * (sl >> 2) + 8 * (sl & 3) + 4 * hA;
@@ -790,8 +793,9 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
             w4[2] = f16_lo2(v.x, v.y, w4[2]);
             w4[3] = f16_lo2(v.z, v.w, w4[3]);
           }
-          qk[sl] = part < 2 ? u32x4{w4[0], w4[1], w4[2], w4[3]} : u32x4{0u, 0u, 0u, 0u};
+          rsm.qkl[wave][sl][hA][row] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
+        wave_lds_sync();
       }
       // Two halves of 32 keys.  The MFMA token-major pass gives lane
       // (t32, hf) the channels {32mb + 8(r/4) + 4hf + r%4} of key 32ht + t32:
@@ -868,7 +872,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
             const u32x4 bh = u32x4{h0, h1, h2, h3};
             const u32x4 bl = u32x4{f16_lo2(kx[0], kx[1], h0), f16_lo2(kx[2], kx[3], h1),
                                    f16_lo2(ky[0], ky[1], h2), f16_lo2(ky[2], ky[3], h3)};
-            const v8h qa = __builtin_bit_cast(v8h, qk[4 * pm + g4]);
+            const v8h qa = __builtin_bit_cast(v8h, rsm.qkl[wave][4 * pm + g4][hf][lane & 7]);
             dq = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, __builtin_bit_cast(v8h, bh), dq, 0, 0, 0);
             dq = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, __builtin_bit_cast(v8h, bl), dq, 0, 0, 0);
           }
