@@ -245,3 +245,46 @@ def test_quantize_prefill_full_size_sampled():
         sl = slice(g * G, (g + 1) * G)
         check_dq_sequence(xg, C4, codes[s, sl].cpu().numpy(), meta[s, sl].cpu().numpy(),
                           recs[s, g:g + 1].cpu().numpy())
+
+
+@pytest.mark.parametrize("m", [4, 8])
+def test_quantize_non_finite_groups_stay_contained(m):
+    """NaN and infinite inputs are outside the contract, but they must not
+    fault and must not leak: every code stays a byte, and the groups without
+    them come out as the oracle computes them (groups are independent)."""
+    G = 128
+    _say(f"quantize non-finite input m={m}")
+    K, _ = synth.kv_numpy(2, 6 * G, 5.0, seed=12, dtype=np.float16)
+    x = K.copy()
+    x[0, 5, 3] = np.nan                      # group 0 of sequence 0
+    x[0, 2 * G + 7] = np.inf                 # group 2: a whole infinite token
+    x[1, 4 * G + 1, 100] = -np.inf           # group 4 of sequence 1
+    x[1, 5 * G:6 * G, 64] = np.nan           # group 5: a channel of NaN
+    bad = {(0, 0), (0, 2), (1, 4), (1, 5)}
+    codes, meta, shift, _, (p, table, C) = quantize_gpu(x, m, G)
+    for s in range(2):
+        for g in range(6):
+            if (s, g) in bad:
+                continue
+            sl = slice(g * G, (g + 1) * G)
+            check_quantized_sequence(x[s, sl].astype(np.float64), C, G, codes[s, sl], meta[s, sl],
+                                     shift[s, g:g + 1])
+    # the same with the double-quantized layout
+    pd = nsnq.Params(sub_dim=m, group_size=G, dq=True)
+    tabd = torch.empty(nsnq.nsn_table_size(pd), dtype=torch.uint8, device=DEV)
+    nsnq.nsn_prepare_codebook(pd, torch.from_numpy(C).to(DEV), tabd)
+    xd = torch.from_numpy(x).to(DEV)
+    cd = torch.empty((2, 6 * G, 128 // m), dtype=torch.uint8, device=DEV)
+    md = torch.empty((2, 6 * G), dtype=torch.float16, device=DEV)
+    rd = torch.empty((2, 6, oracle.record_bytes(G)), dtype=torch.uint8, device=DEV)
+    nsnq.nsn_quantize(pd, xd, tabd, cd, md, rd)
+    torch.cuda.synchronize()
+    from tests.parity import check_dq_sequence
+    C4 = oracle.codebook_4bit(C)
+    for s in range(2):
+        for g in range(6):
+            if (s, g) in bad:
+                continue
+            sl = slice(g * G, (g + 1) * G)
+            check_dq_sequence(x[s, sl].astype(np.float64), C4, cd[s, sl].cpu().numpy(),
+                              md[s, sl].cpu().numpy(), rd[s, g:g + 1].cpu().numpy())
