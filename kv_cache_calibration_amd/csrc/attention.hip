@@ -29,6 +29,12 @@
 //              max it refers to and applied to the group shifts at the end.
 //   The workgroup of chunk 0 first takes the fp16 residual window (exact
 //   scores, original domain), written as partial n_split.
+//   Variants (template flags): ROPE -- keys stored before rotary embedding
+//   (NSNQuant summary §4), scored in the original domain: codewords through
+//   a matrix-core Hadamard, shift, rotation by the key's position, dot
+//   products with the turned queries on the matrix cores; the value side is
+//   unchanged.  DQ -- double-quantized metadata (§3, Double Quantization):
+//   s1 and o' decoded from the 4-bit group records on the fly.
 // attn_combine_kernel: one wave per (batch, query head): log-sum-exp merge of
 //   the chunk partials, inverse rotation, residual partial, normalization.
 #include <type_traits>
