@@ -39,7 +39,9 @@
 //    orders like the distance to within 15 ulp, ties to the lowest code),
 //    keeps the best tile, and the two lane halves of a token settle the
 //    final code.
-// 4. Scale adjustment alpha = ||h||^2 / <h, h_hat>, codes, (s1, s2'), o'.
+// 4. Scale adjustment alpha = ||h||^2 / <h, h_hat>, codes, (s1, s2'), o';
+//    with double quantization (template flag DQ) s2' alone per token and one
+//    4-bit group record of s1 and o' (write_dq_record).
 #include "nsn_device.h"
 #include "nsn_launch.h"
 
