@@ -164,6 +164,10 @@ nsn_status nsn_tune_codebook(int32_t sub_dim, int32_t n_codes, int64_t n_vec,
  * codebook  device, float32 [256][sub_dim] (entries must be finite).
  * table     device, nsn_table_size(p) bytes, written; passed to every
  *           quantize / dequantize / attention call using this codebook.
+ * With NSN_DQ in p->flags the entries are first rounded to the 4-bit levels
+ * given at that flag, and the table holds the rounded codebook; a table is
+ * used with params of the same flags and sub_dim it was prepared with.
+ * Returns NSN_ERR_WORKSPACE when table_bytes < nsn_table_size(p).
  */
 nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook,
                                 void* table, size_t table_bytes,
