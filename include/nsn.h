@@ -79,8 +79,8 @@ typedef enum { NSN_F16 = 0, NSN_F32 = 1 } nsn_dtype;
  *          magnitude, an entry of 0 to +3/16); the search, dequantization
  *          and attention use the rounded codebook.
  * nsn_quantize with this flag takes fp16 input only.  Dequantization and
- * nsn_decode_attention take the decoded values as exact;
- * nsn_decode_attention_rope does not support the flag.  Metadata cost:
+ * the attention calls (with or without rotary keys) take the decoded values
+ * as exact.  Metadata cost:
  * (2 + 136/128) bytes per token, 0.19 bits per value against 0.375 for
  * the fp16 (s1, s2', o') layout. */
 #define NSN_DQ 2u
@@ -315,7 +315,8 @@ nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s,
  * for nsn_decode_attention.
  *
  * rope     host; base finite and > 1, 0 <= q_pos <= 2^40, else
- *          NSN_ERR_INVALID_ARG.  NSN_DQ gives NSN_ERR_UNSUPPORTED.
+ *          NSN_ERR_INVALID_ARG.  With NSN_DQ the cache holds the
+ *          double-quantized layout, as for nsn_decode_attention.
  */
 typedef struct {
   int64_t q_pos;   /* position of the query token */

@@ -87,6 +87,14 @@ struct SplitParams {
   float rope_base;   // rotary base, theta_i = base^(-i/64)
 };
 
+// Double-quantized metadata: per group of the chunk, (lo, step) of the s1
+// grid of keys and of values, and the value shift's scale.
+struct DqSmem {
+  float2 kls[kMaxGroups];
+  float2 vls[kMaxGroups];
+  float vsc[kMaxGroups];
+};
+
 template <int M>
 struct SplitSmem {
   uint32_t cbh[kCodes * M / 2];      // fp16 codebook, 2m bytes per code
@@ -101,6 +109,8 @@ struct SplitSmem {
   uint16_t wrow[kWaves][kTile][16];
   float wm[kWaves][kHB];
   float wl[kWaves][kHB];
+  DqSmem dq;                         // double-quantized metadata (the union's
+                                     // residual half is larger, so free)
 };
 struct ResidSmem {
   float4 sres[kMaxResid];          // per token: scores of the 4 heads (base 2)
@@ -126,14 +136,6 @@ struct RopeSmem {
 struct NoRopeSmem {
   int unused;
 };
-// Double-quantized metadata: per group of the chunk, (lo, step) of the s1
-// grid of keys and of values, and the value shift's scale.
-struct DqSmem {
-  float2 kls[kMaxGroups];
-  float2 vls[kMaxGroups];
-  float vsc[kMaxGroups];
-};
-
 // ds_read_b64_tr_b16: inside each group of 16 lanes, lane 4a + b receives
 // element b of the 8-byte chunks addressed by lanes 4k + a, k = 0..3.  With
 // chunk (lane 4k + a) = 4 channels of token k, lane 4a + b gets one channel
@@ -525,15 +527,14 @@ __device__ void resid_block(const SplitParams& p, ResidSmem& sm, RopeSmem* rs, d
 // each tile's metadata).
 template <int M, int G, bool ROPE, bool DQ>
 __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_kernel(SplitParams p) {
-  static_assert(!(ROPE && DQ), "rotary keys with double quantization are not supported");
   static_assert(!DQ || G == 128, "double quantization uses groups of 128");
   constexpr int CB = kD / M;            // code bytes per token
   constexpr int TPG = G / kTile;        // tiles per group
   constexpr int RB = 2 * kDqRecU16;     // record bytes
   __shared__ AttnSmem<M> smem;
   __shared__ std::conditional_t<ROPE, RopeSmem, NoRopeSmem> rsm;
-  __shared__ std::conditional_t<DQ, DqSmem, NoRopeSmem> dsm;
   SplitSmem<M>& sm = smem.s;
+  DqSmem& dsm = sm.dq;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
   __syncthreads();
   // <q'_h, o'_g> for every group of the chunk, one thread per (g, h)
   if constexpr (DQ) {
-    for (int idx = tid; idx < ng * kHB; idx += kThreads) {
+    for (int idx = tid; idx < (ROPE ? 0 : ng * kHB); idx += kThreads) {
       const int g = idx / kHB, h = idx % kHB;
       const uint8_t* rec = krec + static_cast<int64_t>(g) * RB;
       const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rec + 8);
@@ -739,7 +740,12 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       for (int i = 0; i < CB / 16; ++i)
         kpre[ht][i] = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(kcrow + (tile * kTile + 32 * ht + (lane & 31)) * CB) + i);
-    opre = reinterpret_cast<const uint32_t*>(ksg + static_cast<int64_t>(tile / TPG) * kD)[lane];
+    if constexpr (DQ) {
+      const uint8_t* rec = krec + static_cast<int64_t>(tile / TPG) * RB;
+      opre = static_cast<uint32_t>(rec[8 + lane]) | (static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(rec)[2]) << 16);
+    } else {
+      opre = reinterpret_cast<const uint32_t*>(ksg + static_cast<int64_t>(tile / TPG) * kD)[lane];
+    }
   };
   if constexpr (ROPE) ho = hadamard_ops(lane);
   for (int tau = wave; tau < ntiles; tau += kWaves) {
@@ -760,7 +766,16 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       // lane holding channels 2 lane, 2 lane + 1; the queries turned to the
       // tile's first position
       {
-        float x0 = h2f(opre & 0xffffu), x1 = h2f(opre >> 16);
+        float x0, x1;
+        if constexpr (DQ) {
+          // the o' code byte of channels 2 lane, 2 lane + 1 and the record's scale
+          const float osc = h2f(opre >> 16);
+          x0 = dq_nibble_o(opre & 0xffu, 0, osc);
+          x1 = dq_nibble_o(opre & 0xffu, 1, osc);
+        } else {
+          x0 = h2f(opre & 0xffffu);
+          x1 = h2f(opre >> 16);
+        }
         const float u0 = x0 + x1, u1 = x0 - x1;
         x0 = u0;
         x1 = u1;
@@ -846,7 +861,8 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
         // the result (lane half 0) and 4..7 (half 1) are the high and low
         // query parts of heads 0..3.
         const uint32_t kmt = __shfl(d.km, tok, kWave);
-        const float s1k = h2f(kmt & 0xffffu), s2k = h2f(kmt >> 16);
+        float s1k, s2k;
+        umeta(kmt, tau, false, s1k, s2k);
         const float a = s2k * kInvSqrtD;
         v16f dq = v16f{};
 #pragma unroll
@@ -1138,7 +1154,13 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParam
 template <int M, int G>
 hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s) {
   dim3 grid(a.n_split > 0 ? a.n_split : 1, a.Hkv * sp.hblocks, a.B);
-  if (a.rope && a.dq) return hipErrorInvalidValue;
+  if constexpr (G == 128) {
+    if (a.rope && a.dq) {
+      hipLaunchKernelGGL((attn_split_kernel<M, G, true, true>), grid, dim3(kThreads), 0, s, sp);
+      return hipGetLastError();
+    }
+  }
+  if (a.dq && G != 128) return hipErrorInvalidValue;
   if (a.rope)
     hipLaunchKernelGGL((attn_split_kernel<M, G, true, false>), grid, dim3(kThreads), 0, s, sp);
   else if constexpr (G == 128) {

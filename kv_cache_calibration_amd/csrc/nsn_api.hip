@@ -403,8 +403,6 @@ nsn_status nsn_decode_attention_rope(const nsn_params* p, const nsn_attn_shape* 
     return fail(NSN_ERR_INVALID_ARG, "rope base must be finite and > 1, got %g", static_cast<double>(r->base));
   if (r->q_pos < 0 || r->q_pos > (int64_t(1) << 40))
     return fail(NSN_ERR_INVALID_ARG, "q_pos must lie in [0, 2^40], got %lld", static_cast<long long>(r->q_pos));
-  if (p && (p->flags & NSN_DQ))
-    return fail(NSN_ERR_UNSUPPORTED, "NSN_DQ is not supported with rotary keys");
   return decode_attention_impl(p, s, r, q, k_codes, k_meta, k_shift, v_codes, v_meta, v_shift,
                                k_resid, v_resid, table, workspace, workspace_bytes, out, stream,
                                "nsn_decode_attention_rope launch");

@@ -227,12 +227,12 @@ def test_double_quantization_validation(lib):
              NULL) == _lib.NSN_ERR_INVALID_ARG
     assert f(P(G=256, flags=DQ), FAKE, 256 * 32, FAKE, 256, FAKE, 136, FAKE, 2, 256, 0, FAKE,
              256 * 128, NULL) == _lib.NSN_ERR_UNSUPPORTED
-    # rotary keys are not supported with it
+    # groups of 128 only, with rotary keys too
     s = _shape()
     r = _lib.nsn_rope(10, 10000.0)
     args = [FAKE] * 10
-    st = lib.nsn_decode_attention_rope(P(flags=DQ), ctypes.byref(s), ctypes.byref(r), *args, FAKE,
-                                       1 << 30, FAKE, NULL)
+    st = lib.nsn_decode_attention_rope(P(G=256, flags=DQ), ctypes.byref(s), ctypes.byref(r), *args,
+                                       FAKE, 1 << 30, FAKE, NULL)
     assert st == _lib.NSN_ERR_UNSUPPORTED
     assert lib.nsn_decode_attention_workspace_size(P(flags=DQ), ctypes.byref(s)) > 0
     assert lib.nsn_decode_attention_workspace_size(P(G=256, flags=DQ), ctypes.byref(s)) == 0

@@ -301,3 +301,43 @@ def test_attention_dq_largest_chunk_sampled():
                                        cache["vr"][b:b + 1, kvh:kvh + 1].cpu().numpy(), C4, G, Nq, R,
                                        scale)
         assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
+
+
+def run_dq_attention_rope(cache, q, scale, q_pos, base):
+    B, Hq, _ = q.shape
+    p = cache["p"]
+    ws = nsnq.nsn_decode_attention_workspace_size(p, B, Hq, cache["Hkv"], cache["Nq"], cache["R"],
+                                                  cache["k"][0].shape[2], cache["kr"].shape[2], scale)
+    work = torch.empty(max(ws, 16), dtype=torch.uint8, device=DEV)
+    out = torch.full((B, Hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    nsnq.nsn_decode_attention_rope(p, q, cache["k"], cache["v"], cache["kr"], cache["vr"],
+                                   cache["table"], work, out, cache["Nq"], cache["R"], scale,
+                                   q_pos, base)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,R,m,dpos,base", [
+    (2, 8, 2, 1024, 16, 4, 0, 10000.0),       # GQA 4:1, query at the last residual position
+    (1, 4, 1, 2048, 64, 8, 0, 10000.0),       # 1-bit codes
+    (1, 16, 2, 3072, 5, 4, 777, 500000.0),    # two head blocks, another base, query ahead
+    (1, 4, 1, 10240, 7, 4, 123456, 10000.0),  # several chunks, large positions
+    (1, 3, 1, 128, 200, 4, 0, 10000.0),       # one group, long residual
+])
+def test_attention_dq_rope_parity(B, Hq, Hkv, Nq, R, m, dpos, base):
+    """Keys stored before rotary embedding with double-quantized metadata:
+    against the oracle's rotary attention over the decoded records."""
+    _say(f"attention DQ + RoPE B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} R={R} m={m} dpos={dpos}")
+    cache = build_dq_cache(B, Hkv, Nq, R, m, seed=61)
+    q = synth.query_torch((B, Hq, 128), seed=62, device=DEV)
+    scale = 1.0 / math.sqrt(128)
+    q_pos = Nq + R - 1 + dpos
+    got = run_dq_attention_rope(cache, q, scale, q_pos, base)
+    k = _decoded(cache["k"], B, Hkv)
+    v = _decoded(cache["v"], B, Hkv)
+    want = oracle.decode_attention_rope(q.cpu().numpy(), k, v, cache["kr"].cpu().numpy(),
+                                        cache["vr"].cpu().numpy(), cache["C4"], G, Nq, R, scale,
+                                        q_pos, base)
+    err = np.abs(got - want).max()
+    assert err <= ATTN_ABS, err
+    assert rel_l2(got, want) < 2e-3
