@@ -340,6 +340,20 @@ def main():
             evad.append((a, b))
     torch.cuda.synchronize()
     ms_attn_dq = float(np.mean([a.elapsed_time(b) for a, b in evad]))
+    # the same double-quantized caches read as keys stored before rotary
+    # embedding (query at the last residual position)
+    evadr = []
+    for i in range(max(args.steps, 3) + 1):
+        kcq, vcq, krq, vrq, qq = cachesq[i % 3]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nsnq.nsn_decode_attention_rope(pq, qq, kcq, vcq, krq, vrq, tableq, work, out, Nq, R, scale,
+                                       Nq + R - 1, ROPE_BASE)
+        b.record(stream)
+        if i > 0:
+            evadr.append((a, b))
+    torch.cuda.synchronize()
+    ms_attn_dq_rope = float(np.mean([a.elapsed_time(b) for a, b in evadr]))
     del cachesq
 
     qb = quant_bytes(n_seq, T, m, G)
@@ -365,6 +379,8 @@ def main():
         "quantize_dq_ms": ms_qdq,
         "attention_dq_gbps": attn_bytes_dq(B3, Hq, Hkv, Nq, R, m, G) / (ms_attn_dq * 1e-3) / 1e9,
         "attention_dq_ms": ms_attn_dq,
+        "attention_dq_rope_gbps": attn_bytes_dq(B3, Hq, Hkv, Nq, R, m, G) / (ms_attn_dq_rope * 1e-3) / 1e9,
+        "attention_dq_rope_ms": ms_attn_dq_rope,
         "flush_gbps": fb / (ms["flush"] * 1e-3) / 1e9,
         "dequantize_gbps": db / (ms["dequantize"] * 1e-3) / 1e9,
     }
@@ -375,6 +391,7 @@ def main():
     rates["attention_rope_frac_hbm"] = rates["attention_rope_gbps"] / HBM_PEAK_GBPS
     rates["quantize_dq_frac_hbm"] = rates["quantize_dq_gbps"] / HBM_PEAK_GBPS
     rates["attention_dq_frac_hbm"] = rates["attention_dq_gbps"] / HBM_PEAK_GBPS
+    rates["attention_dq_rope_frac_hbm"] = rates["attention_dq_rope_gbps"] / HBM_PEAK_GBPS
     log("kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ms.items()))
     log("rates: " + ", ".join(f"{k} {v:.4g}" for k, v in rates.items()))
 
