@@ -39,6 +39,7 @@ __all__ = [
     "nsn_decode_attention_rope",
     "nsn_decode_attention_workspace_size",
     "lib_path",
+    "cache_layout",
 ]
 
 
@@ -115,6 +116,20 @@ def _inner_contig(t, inner):
         if t.shape[d] > 1 and t.stride(d) != st:
             raise ValueError("inner dimensions must be contiguous")
         st *= t.shape[d]
+
+
+def cache_layout(params, n_seq, cap):
+    """Shapes and torch dtypes of (codes, meta, shift) for n_seq sequences of
+    cap token slots in the layout ``params`` selects (plain or double
+    quantized); cap is a multiple of the group size."""
+    import torch
+    G, m = params.group_size, params.sub_dim
+    if cap % G:
+        raise ValueError("cap must be a multiple of group_size")
+    codes = ((n_seq, cap, 128 // m), torch.uint8)
+    if params.dq:
+        return codes, ((n_seq, cap), torch.float16), ((n_seq, cap // G, 136), torch.uint8)
+    return codes, ((n_seq, cap, 2), torch.float16), ((n_seq, cap // G, 128), torch.float16)
 
 
 def nsn_table_size(params):

@@ -296,3 +296,19 @@ def test_binding_layout_checks_of_both_metadata_layouts():
         nsnq._check_attention_shapes(p, q, plain, plain, kr, kr[:, :, :8], out)
     with pytest.raises(ValueError):
         nsnq._check_attention_shapes(nsnq.Params(sub_dim=8), q, plain, plain, kr, kr, out)
+
+
+def test_cache_layout_helper():
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    c, m, s = nsnq.cache_layout(nsnq.Params(sub_dim=4), 3, 256)
+    assert c == ((3, 256, 32), torch.uint8) and m == ((3, 256, 2), torch.float16)
+    assert s == ((3, 2, 128), torch.float16)
+    c, m, s = nsnq.cache_layout(nsnq.Params(sub_dim=8, dq=True), 3, 256)
+    assert c == ((3, 256, 16), torch.uint8) and m == ((3, 256), torch.float16)
+    assert s == ((3, 2, 136), torch.uint8)
+    meta = torch.zeros(m[0], dtype=m[1])
+    shift = torch.zeros(s[0], dtype=s[1])
+    nsnq._check_meta_layout(nsnq.Params(sub_dim=8, dq=True), meta, shift)
+    with pytest.raises(ValueError):
+        nsnq.cache_layout(nsnq.Params(), 1, 100)
