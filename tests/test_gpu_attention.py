@@ -171,3 +171,25 @@ def test_attention_largest_chunk_sampled(m, G):
         want = oracle.decode_attention(qn[b:b + 1, h:h + 1], k, v, sl(cache["kr"]), sl(cache["vr"]),
                                        cache["C"], G, Nq, R, scale)
         assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
+
+
+@pytest.mark.parametrize("m,G", [(4, 128), (8, 256)])
+def test_attention_partly_filled_cache_and_residual(m, G):
+    """The serving case: the cache rows have room for more groups than are
+    filled (cache_capacity > n_quant_tok) and the residual window is partly
+    filled (resid_capacity 128, 37 valid); the unused slots hold garbage that
+    must not be read."""
+    B, Hq, Hkv, Nq, R = 2, 8, 2, 4 * G, 37
+    cap, rcap = Nq + 3 * G, 128
+    print(f"attention partly filled m={m} G={G}", flush=True)
+    cache = build_cache(B, Hkv, Nq, R, m, G, seed=91, cap=cap, rcap=rcap)
+    # garbage in the unused slots: NaN metadata and residual tokens, random codes
+    for part in (cache["k"], cache["v"]):
+        part[0][:, :, Nq:] = torch.randint(0, 256, part[0][:, :, Nq:].shape, dtype=torch.uint8, device=DEV)
+        part[1][:, :, Nq:] = float("nan")
+        part[2][:, :, Nq // G:] = float("nan")
+    cache["kr"][:, :, R:] = float("nan")
+    cache["vr"][:, :, R:] = float("nan")
+    q = synth.query_torch((B, Hq, 128), seed=92, device=DEV)
+    err = check(cache, q)
+    assert np.isfinite(err)

@@ -341,3 +341,36 @@ def test_attention_dq_rope_parity(B, Hq, Hkv, Nq, R, m, dpos, base):
     err = np.abs(got - want).max()
     assert err <= ATTN_ABS, err
     assert rel_l2(got, want) < 2e-3
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_attention_dq_partly_filled_cache_and_residual(rope):
+    """Double-quantized cache rows with room for three more groups than are
+    filled and a partly filled residual; the unused slots hold garbage (NaN
+    s2' and records, random codes, NaN residual tokens) that must not be
+    read, with and without rotary keys."""
+    B, Hq, Hkv, Nq, R, m = 2, 8, 2, 512, 37, 4
+    cap, rcap = Nq + 3 * G, 128
+    _say(f"attention DQ partly filled rope={rope}")
+    cache = build_dq_cache(B, Hkv, Nq, R, m, seed=93, cap=cap, rcap=rcap)
+    for part in (cache["k"], cache["v"]):
+        part[0][:, :, Nq:] = torch.randint(0, 256, part[0][:, :, Nq:].shape, dtype=torch.uint8, device=DEV)
+        part[1][:, :, Nq:] = float("nan")
+        part[2][:, :, Nq // G:] = 0xFF
+    cache["kr"][:, :, R:] = float("nan")
+    cache["vr"][:, :, R:] = float("nan")
+    q = synth.query_torch((B, Hq, 128), seed=94, device=DEV)
+    scale = 1.0 / math.sqrt(128)
+    k = _decoded(cache["k"], B, Hkv)
+    v = _decoded(cache["v"], B, Hkv)
+    kr, vr = cache["kr"].cpu().numpy(), cache["vr"].cpu().numpy()
+    if rope:
+        q_pos = Nq + R - 1
+        got = run_dq_attention_rope(cache, q, scale, q_pos, 10000.0)
+        want = oracle.decode_attention_rope(q.cpu().numpy(), k, v, kr, vr, cache["C4"], G, Nq, R, scale,
+                                            q_pos, 10000.0)
+    else:
+        got = run_dq_attention(cache, q, scale)
+        want = oracle.decode_attention(q.cpu().numpy(), k, v, kr, vr, cache["C4"], G, Nq, R, scale)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= ATTN_ABS
