@@ -193,3 +193,16 @@ def test_attention_partly_filled_cache_and_residual(m, G):
     q = synth.query_torch((B, Hq, 128), seed=92, device=DEV)
     err = check(cache, q)
     assert np.isfinite(err)
+
+
+def test_attention_long_context_many_chunks():
+    """One (batch, kv head) row of 131072 quantized tokens: 256 chunks of 512
+    for one head block, so the merge combines 257 partials."""
+    B, Hq, Hkv, Nq, R, m, G = 1, 4, 1, 131072, 5, 4, 128
+    print("attention long context: 131072 tokens, one row", flush=True)
+    cache = build_cache(B, Hkv, Nq, R, m, G, seed=95, device_gen=True)
+    scale = 1 / math.sqrt(128)
+    ws = nsnq.nsn_decode_attention_workspace_size(cache["p"], B, Hq, Hkv, Nq, R, Nq, R, scale)
+    assert ws == B * Hq * (256 + 1) * 132 * 4
+    q = synth.query_torch((B, Hq, 128), seed=96, device=DEV)
+    check(cache, q)
