@@ -14,7 +14,9 @@
  * Conventions for every call
  *  - Pointers documented "device" are HIP device memory owned by the caller;
  *    the library never allocates, frees or retains them.  Every device
- *    pointer must be 16-byte aligned.
+ *    pointer must be 16-byte aligned, except that with NSN_DQ the shift
+ *    (group record) pointers need only 8 (records are 136 bytes, so a
+ *    cache advanced by an odd number of groups is 8-byte aligned).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream) and never synchronize.  Kernel faults surface at the caller's
  *    next synchronization.

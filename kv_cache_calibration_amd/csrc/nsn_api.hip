@@ -37,6 +37,11 @@ nsn_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// The shift argument: 16 bytes, or 8 with NSN_DQ (the 136-byte group records
+// are 8-byte aligned, so a cache advanced by an odd number of groups is too).
+bool shift_aligned(const nsn_params* p, const void* q) {
+  return (reinterpret_cast<uintptr_t>(q) & ((p->flags & NSN_DQ) ? 7u : 15u)) == 0;
+}
 
 nsn_status check_params(const nsn_params* p) {
   if (!p) return fail(NSN_ERR_INVALID_ARG, "params is NULL");
@@ -208,7 +213,7 @@ nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype, const void* x, 
   const int64_t esz = in_dtype == NSN_F16 ? 2 : 4;
   if (!x || !table || !codes || !meta || !shift)
     return fail(NSN_ERR_INVALID_ARG, "x, table, codes, meta and shift must be non-NULL");
-  if (!aligned16(x) || !aligned16(table) || !aligned16(codes) || !aligned16(meta) || !aligned16(shift))
+  if (!aligned16(x) || !aligned16(table) || !aligned16(codes) || !aligned16(meta) || !shift_aligned(p, shift))
     return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   if (n_seq > 1) {
     if (x_seq_stride < n_tok * 128 || (x_seq_stride * esz) % 16)
@@ -246,7 +251,7 @@ nsn_status nsn_dequantize(const nsn_params* p, const uint8_t* codes, int64_t cod
   const int64_t esz = out_dtype == NSN_F16 ? 2 : 4;
   if (!x_hat || !table || !codes || !meta || !shift)
     return fail(NSN_ERR_INVALID_ARG, "codes, meta, shift, table and x_hat must be non-NULL");
-  if (!aligned16(x_hat) || !aligned16(table) || !aligned16(codes) || !aligned16(meta) || !aligned16(shift))
+  if (!aligned16(x_hat) || !aligned16(table) || !aligned16(codes) || !aligned16(meta) || !shift_aligned(p, shift))
     return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   if (n_seq > 1) {
     if (out_seq_stride < n_tok * 128 || (out_seq_stride * esz) % 16)
@@ -337,10 +342,11 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
     return fail(NSN_ERR_INVALID_ARG, "cache arrays must be non-NULL when n_quant_tok > 0");
   if (s->n_resid_tok > 0 && (!k_resid || !v_resid))
     return fail(NSN_ERR_INVALID_ARG, "residual arrays must be non-NULL when n_resid_tok > 0");
-  const void* ptrs[] = {q, k_codes, k_meta, k_shift, v_codes, v_meta, v_shift,
-                        k_resid, v_resid, table, workspace, out};
+  const void* ptrs[] = {q, k_codes, k_meta, v_codes, v_meta, k_resid, v_resid, table, workspace, out};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if ((k_shift && !shift_aligned(p, k_shift)) || (v_shift && !shift_aligned(p, v_shift)))
+    return fail(NSN_ERR_INVALID_ARG, "shift pointers must be 16-byte aligned (8 with NSN_DQ)");
   int n_split = 0, chunk = 0;
   nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, p->group_size, &n_split,
                  &chunk);

@@ -227,6 +227,10 @@ def test_double_quantization_validation(lib):
              NULL) == _lib.NSN_ERR_INVALID_ARG
     assert f(P(G=256, flags=DQ), FAKE, 256 * 32, FAKE, 256, FAKE, 136, FAKE, 2, 256, 0, FAKE,
              256 * 128, NULL) == _lib.NSN_ERR_UNSUPPORTED
+    # group records are 8-byte aligned, so with NSN_DQ the shift pointer needs
+    # only 8-byte alignment; 4 is still rejected, and 8 without the flag
+    assert _q(lib, P(flags=DQ), ms=256, ss=2 * 68, shift=ctypes.c_void_p(0x10004)) == _lib.NSN_ERR_INVALID_ARG
+    assert _q(lib, P(), shift=ctypes.c_void_p(0x10008)) == _lib.NSN_ERR_INVALID_ARG
     # groups of 128 only, with rotary keys too
     s = _shape()
     r = _lib.nsn_rope(10, 10000.0)

@@ -85,13 +85,16 @@ def test_quantize_dq_parity(m, n_seq, T):
     _say(f"  {ties} code near-ties of {total}, {near} record near-ties, {hdr} headers off by an ulp")
 
 
-def test_quantize_dq_strided_into_cache():
+@pytest.mark.parametrize("off_groups", [4, 3])
+def test_quantize_dq_strided_into_cache(off_groups):
     """Two sequences, three groups each, written at a group offset inside
-    larger caches; nothing outside the written slots changes."""
+    larger caches (an odd offset leaves the record pointer 8-byte aligned);
+    nothing outside the written slots changes, and dequantization from the
+    same offset reads them back."""
     m = 4
     K, _ = synth.kv_numpy(2, 3 * G, 5.0, seed=5, dtype=np.float16)
     p, table, C4 = dq_table(m)
-    cap, off = 9 * G, 4 * G
+    cap, off = 9 * G, off_groups * G
     codes, meta, recs = alloc_dq(2, cap, m)
     x = torch.from_numpy(K).to(DEV)
     nsnq.nsn_quantize(p, x, table, codes[:, off:], meta[:, off:], recs[:, off // G:])
@@ -103,6 +106,14 @@ def test_quantize_dq_strided_into_cache():
     for s in range(2):
         check_dq_sequence(K[s].astype(np.float64), C4, c[s, off:off + 3 * G], mt[s, off:off + 3 * G],
                           rc[s, off // G:off // G + 3])
+    out = torch.empty((2, 3 * G, 128), dtype=torch.float32, device=DEV)
+    nsnq.nsn_dequantize(p, codes[:, off:], meta[:, off:], recs[:, off // G:], table, out, n_tok=3 * G)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for s in range(2):
+        m2, s2 = oracle.dq_unpack(mt[s, off:off + 3 * G], rc[s, off // G:off // G + 3], G)
+        want = oracle.dequantize(c[s, off:off + 3 * G], m2, s2, C4, G)
+        assert rel_l2(got[s], want) <= SAME_BYTES_REL
 
 
 def test_quantize_dq_degenerate_groups():
