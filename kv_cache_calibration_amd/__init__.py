@@ -192,8 +192,20 @@ def nsn_nearest_codeword(params, table, v, out, stream=None):
     n = v.numel() // params.sub_dim
     if out.numel() < n:
         raise ValueError("out too small")
+    _check_table(params, table)
     _lib.check(_lib.load().nsn_nearest_codeword(ctypes.byref(params.c), _ptr(table), _ptr(v), n,
                                                 _ptr(out), _stream(stream)))
+
+
+def _check_table(params, table):
+    if table.numel() * table.element_size() < nsn_table_size(params):
+        raise ValueError("table is smaller than nsn_table_size(params)")
+
+
+def _check_codes(params, codes):
+    import torch
+    if codes.dtype != torch.uint8 or codes.shape[-1] != 128 // params.sub_dim:
+        raise ValueError(f"codes must be uint8 with {128 // params.sub_dim} bytes per token")
 
 
 def _dtype_code(t):
@@ -217,6 +229,10 @@ def nsn_quantize(params, x, table, codes, meta, shift, n_tok=None, stream=None):
     _inner_contig(meta, None)
     _inner_contig(shift, None)
     _check_meta_layout(params, meta, shift)
+    _check_codes(params, codes)
+    _check_table(params, table)
+    if x.shape[1] < n_tok or codes.shape[1] < n_tok or meta.shape[1] < n_tok:
+        raise ValueError("n_tok exceeds the tensors' token dimension")
     lib = _lib.load()
     _lib.check(lib.nsn_quantize(ctypes.byref(params.c), _dtype_code(x), _ptr(x), x.shape[0], n_tok,
                                 x.stride(0), _ptr(table), _ptr(codes), codes.stride(0), _ptr(meta),
@@ -231,6 +247,10 @@ def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=No
     _inner_contig(meta, None)
     _inner_contig(shift, None)
     _check_meta_layout(params, meta, shift)
+    _check_codes(params, codes)
+    _check_table(params, table)
+    if codes.shape[1] < n_tok or meta.shape[1] < n_tok or out.shape[1] < n_tok:
+        raise ValueError("n_tok exceeds the tensors' token dimension")
     lib = _lib.load()
     _lib.check(lib.nsn_dequantize(ctypes.byref(params.c), _ptr(codes), codes.stride(0), _ptr(meta),
                                   _stride16(meta), _ptr(shift), _stride16(shift), _ptr(table),
@@ -241,8 +261,11 @@ def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=No
 def nsn_residual_append(tok, resid, pos, stream=None):
     """tok fp16 (n_seq, 128); resid fp16 (n_seq, cap, 128)."""
     _dev(tok, resid)
+    import torch
     if not tok.is_contiguous():
         raise ValueError("tok must be contiguous")
+    if tok.dtype != torch.float16 or resid.dtype != torch.float16 or tuple(tok.shape) != (resid.shape[0], 128):
+        raise ValueError("tok must be fp16 (n_seq, 128) and resid fp16 (n_seq, cap, 128)")
     _inner_contig(resid, (resid.shape[1], 128))
     lib = _lib.load()
     _lib.check(lib.nsn_residual_append(_ptr(tok), tok.shape[0], _ptr(resid), resid.stride(0),
@@ -293,10 +316,15 @@ def _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out):
     kc = k_cache[0]
     Hkv, cap = kc.shape[1], kc.shape[2]
     G = params.group_size
+    import torch
     if tuple(q.shape) != (B, Hq, 128) or tuple(out.shape) != (B, Hq, 128):
         raise ValueError("q and out must be (B, Hq, 128)")
+    if q.dtype != torch.float16 or out.dtype != torch.float32:
+        raise ValueError("q must be fp16 and out fp32")
+    if k_resid.dtype != torch.float16 or v_resid.dtype != torch.float16:
+        raise ValueError("residuals must be fp16")
     for c, mt, sh in (k_cache, v_cache):
-        if tuple(c.shape) != (B, Hkv, cap, 128 // params.sub_dim):
+        if tuple(c.shape) != (B, Hkv, cap, 128 // params.sub_dim) or c.dtype != torch.uint8:
             raise ValueError("codes must be (B, Hkv, cap, 128 // m), alike for K and V")
         if params.dq:
             ok = (tuple(mt.shape) == (B, Hkv, cap) and mt.element_size() == 2 and
@@ -323,6 +351,7 @@ def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, work
     B, Hq, _ = q.shape
     Hkv, cap = kc.shape[1], kc.shape[2]
     _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out)
+    _check_table(params, table)
     s = _shape(B, Hq, Hkv, n_quant_tok, n_resid_tok, cap, k_resid.shape[2], softmax_scale)
     lib = _lib.load()
     bufs = (_ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc), _ptr(vm), _ptr(vs), _ptr(k_resid),

@@ -316,3 +316,30 @@ def test_cache_layout_helper():
     nsnq._check_meta_layout(nsnq.Params(sub_dim=8, dq=True), meta, shift)
     with pytest.raises(ValueError):
         nsnq.cache_layout(nsnq.Params(), 1, 100)
+
+
+def test_binding_rejects_wrong_dtypes_and_sizes():
+    """The binding checks what the C ABI cannot see: dtypes, the table size
+    and token counts (host tensors suffice; the checks run before any call)."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    p = nsnq.Params(sub_dim=4)
+    with pytest.raises(ValueError):
+        nsnq._check_codes(p, torch.zeros((2, 256, 16), dtype=torch.uint8))   # 1-bit width for 2-bit params
+    with pytest.raises(ValueError):
+        nsnq._check_codes(p, torch.zeros((2, 256, 32), dtype=torch.int16))
+    nsnq._check_codes(p, torch.zeros((2, 256, 32), dtype=torch.uint8))
+    B, Hq, Hkv, cap, R = 1, 4, 1, 128, 4
+    kc = torch.zeros((B, Hkv, cap, 32), dtype=torch.uint8)
+    plain = (kc, torch.zeros((B, Hkv, cap, 2), dtype=torch.float16),
+             torch.zeros((B, Hkv, 1, 128), dtype=torch.float16))
+    kr = torch.zeros((B, Hkv, R, 128), dtype=torch.float16)
+    q = torch.zeros((B, Hq, 128), dtype=torch.float16)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32)
+    nsnq._check_attention_shapes(p, q, plain, plain, kr, kr, out)
+    with pytest.raises(ValueError):
+        nsnq._check_attention_shapes(p, q.float(), plain, plain, kr, kr, out)
+    with pytest.raises(ValueError):
+        nsnq._check_attention_shapes(p, q, plain, plain, kr, kr, out.half())
+    with pytest.raises(ValueError):
+        nsnq._check_attention_shapes(p, q, plain, plain, kr.float(), kr, out)
