@@ -58,6 +58,7 @@ constexpr int kMaxResid = 1024;
 constexpr int kPartStride = 132;     // acc[128], m, l, pad
 constexpr int kBlocksPerCU = 4;      // split workgroups one CU can hold (<= 128 VGPRs)
 constexpr int kPlanBlocksPerCU = 3;  // workgroups per CU the split count aims at (measured best)
+constexpr int kPlanBlocksPerCURope = 2;  // the rotary kernel: two fit per CU (LDS, registers)
 constexpr int kPlanCUs = 256;
 constexpr float kInvSqrtD = 0.08838834764831845f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1177,7 +1178,7 @@ hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s)
 
 }  // namespace
 
-void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int* n_split, int* chunk) {
+void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int rope, int* n_split, int* chunk) {
   if (n_quant <= 0) {
     *n_split = 0;
     *chunk = 0;
@@ -1187,7 +1188,7 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int* n_split
   const int64_t units = static_cast<int64_t>(B) * Hkv * ((grp + kHB - 1) / kHB);
   // about three workgroups per CU in one round: every CU equally busy, with
   // room left for one more workgroup per CU while the others finish
-  const int64_t slots = static_cast<int64_t>(kPlanCUs) * kPlanBlocksPerCU;
+  const int64_t slots = static_cast<int64_t>(kPlanCUs) * (rope ? kPlanBlocksPerCURope : kPlanBlocksPerCU);
   int64_t want = slots / units;
   const int64_t max_split = (n_quant + kMinChunk - 1) / kMinChunk;
   if (want > max_split) want = max_split;

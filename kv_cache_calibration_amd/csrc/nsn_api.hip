@@ -322,7 +322,7 @@ static nsn_status check_attn(const nsn_params* p, const nsn_attn_shape* s) {
 size_t nsn_decode_attention_workspace_size(const nsn_params* p, const nsn_attn_shape* s) {
   if (check_attn(p, s) != NSN_OK) return 0;
   int n_split = 0, chunk = 0;
-  nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, p->group_size, &n_split,
+  nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, p->group_size, 0, &n_split,
                  &chunk);
   return nsn::attn_workspace_bytes(s->batch, s->n_q_heads, n_split);
 }
@@ -348,8 +348,8 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
   if ((k_shift && !shift_aligned(p, k_shift)) || (v_shift && !shift_aligned(p, v_shift)))
     return fail(NSN_ERR_INVALID_ARG, "shift pointers must be 16-byte aligned (8 with NSN_DQ)");
   int n_split = 0, chunk = 0;
-  nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, p->group_size, &n_split,
-                 &chunk);
+  nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, p->group_size, r ? 1 : 0,
+                 &n_split, &chunk);
   const size_t need = nsn::attn_workspace_bytes(s->batch, s->n_q_heads, n_split);
   if (workspace_bytes < need)
     return fail(NSN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);

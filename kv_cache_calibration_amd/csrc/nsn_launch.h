@@ -85,8 +85,10 @@ struct AttnArgs {
   int64_t q_pos;     // query position (rope = 1)
   int dq;            // 1: double-quantized metadata (group_size 128)
 };
-// Split choice shared by the workspace-size query and the launch.
-void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size,
+// Split choice shared by the workspace-size query and the launch; the
+// rotary kernel (rope = 1) aims at fewer workgroups per CU, so it never needs
+// more workspace than the plain plan the size query reports.
+void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int rope,
                int* n_split, int* chunk);
 size_t attn_workspace_bytes(int B, int Hq, int n_split);
 hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s);
