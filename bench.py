@@ -44,6 +44,13 @@ DQ_REC = 136   # bytes of a double-quantized group record (G = 128)
 TUNE_ITERS, TUNE_LR = 20, 3e-3
 
 
+def side_ms(events):
+    """Median launch time (ms) of a side measurement: its launches run on an
+    otherwise idle stream, so one late launch must not move the figure."""
+    import numpy as np
+    return float(np.median([a.elapsed_time(b) for a, b in events]))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -265,7 +272,7 @@ def main():
         if i > 0:
             ev1.append((a, b))
     torch.cuda.synchronize()
-    ms_attn1 = float(np.mean([a.elapsed_time(b) for a, b in ev1]))
+    ms_attn1 = side_ms(ev1)
 
     # side measurement, outside the step: the 2-bit decode attention with the
     # keys stored before rotary embedding (query at the last residual position)
@@ -280,7 +287,7 @@ def main():
         if i > 0:
             evr.append((a, b))
     torch.cuda.synchronize()
-    ms_attn_rope = float(np.mean([a.elapsed_time(b) for a, b in evr]))
+    ms_attn_rope = side_ms(evr)
 
     # side measurement, outside the step: the same prefill quantize with
     # 1-bit codes (its metadata and shifts overwrite the step's outputs)
@@ -294,7 +301,7 @@ def main():
         if i > 0:
             evq1.append((a, b))
     torch.cuda.synchronize()
-    ms_q1 = float(np.mean([a.elapsed_time(b) for a, b in evq1]))
+    ms_q1 = side_ms(evq1)
     del codes1
 
     # side measurements, outside the step: double-quantized metadata (4-bit
@@ -315,7 +322,7 @@ def main():
         if i > 0:
             evqd.append((a, b))
     torch.cuda.synchronize()
-    ms_qdq = float(np.mean([a.elapsed_time(b) for a, b in evqd]))
+    ms_qdq = side_ms(evqd)
     del meta_q, recs_q
     cachesq = []
     for c in range(3):
@@ -339,7 +346,7 @@ def main():
         if i > 0:
             evad.append((a, b))
     torch.cuda.synchronize()
-    ms_attn_dq = float(np.mean([a.elapsed_time(b) for a, b in evad]))
+    ms_attn_dq = side_ms(evad)
     # the same double-quantized caches read as keys stored before rotary
     # embedding (query at the last residual position)
     evadr = []
@@ -353,7 +360,7 @@ def main():
         if i > 0:
             evadr.append((a, b))
     torch.cuda.synchronize()
-    ms_attn_dq_rope = float(np.mean([a.elapsed_time(b) for a, b in evadr]))
+    ms_attn_dq_rope = side_ms(evadr)
     del cachesq
 
     qb = quant_bytes(n_seq, T, m, G)
