@@ -46,10 +46,16 @@ typedef enum {
   NSN_ERR_INVALID_ARG = 1,
   NSN_ERR_UNSUPPORTED = 2,
   NSN_ERR_WORKSPACE = 3,
-  NSN_ERR_HIP = 4
+  NSN_ERR_HIP = 4,
+  NSN_ERR_INTERNAL = 5,  /* a library invariant failed (a bug); nothing launched */
+  NSN_STATUS_MAX_ENUM = 0x7fffffff   /* not a status: makes every int value valid */
 } nsn_status;
 
-typedef enum { NSN_F16 = 0, NSN_F32 = 1 } nsn_dtype;
+typedef enum {
+  NSN_F16 = 0,
+  NSN_F32 = 1,
+  NSN_DTYPE_MAX_ENUM = 0x7fffffff    /* not a dtype: makes every int value valid */
+} nsn_dtype;
 
 /* nsn_params.flags: per-token scale adjustment (NSNQuant summary, §3:
  * the quantized vector is rescaled so that its component along the
@@ -96,7 +102,8 @@ typedef struct {
 } nsn_params;
 
 /* Size in bytes of a prepared codebook for these params (codebook, squared
- * norms and search tables); constant for the supported shapes. */
+ * norms and search tables); constant for the supported shapes, 0 for
+ * invalid or unsupported params. */
 size_t nsn_table_size(const nsn_params* p);
 
 /*
@@ -113,7 +120,8 @@ size_t nsn_table_size(const nsn_params* p);
  * in sample order (a centroid with no members keeps its value).  The final
  * centroids are rounded to the nearest fp16 value (ties to even) and stored
  * as float32.  Deterministic.
- * workspace device, >= nsn_build_codebook_workspace_size() bytes.
+ * workspace device, >= nsn_build_codebook_workspace_size() bytes (the
+ *           query returns 0 for arguments outside the requirements).
  * Requires n_codes == 256, sub_dim in {4, 8}, n_codes <= n_samples
  * <= 2^26, 1 <= iters <= 1000.
  */
@@ -163,12 +171,18 @@ nsn_status nsn_tune_codebook(int32_t sub_dim, int32_t n_codes, int64_t n_vec,
 
 /*
  * nsn_prepare_codebook -- derive the device search tables from a codebook.
- * codebook  device, float32 [256][sub_dim] (entries must be finite).
+ * codebook  device, float32 [256][sub_dim]; entries must be finite with
+ *           |c| <= 65504 (the fp16 range).
  * table     device, nsn_table_size(p) bytes, written; passed to every
  *           quantize / dequantize / attention call using this codebook.
- * With NSN_DQ in p->flags the entries are first rounded to the 4-bit levels
- * given at that flag, and the table holds the rounded codebook; a table is
- * used with params of the same flags and sub_dim it was prepared with.
+ * Every entry is first rounded once: to the nearest fp16 value (ties to
+ * even), or with NSN_DQ in p->flags to the 4-bit level given at that flag.
+ * The table holds only the rounded codebook, and the search, the scale
+ * adjustment, dequantization and attention all use it (a codebook from
+ * nsn_build_codebook or nsn_tune_codebook is already fp16-valued and passes
+ * unchanged).  A table is used with params of the same flags and sub_dim it
+ * was prepared with; the table lives in device memory, so a mismatch is not
+ * detected.
  * Returns NSN_ERR_WORKSPACE when table_bytes < nsn_table_size(p).
  */
 nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook,
@@ -182,7 +196,8 @@ nsn_status nsn_prepare_codebook(const nsn_params* p, const float* codebook,
  *  codeword in one global codebook.]
  * v      device float32 [n][sub_dim]; out device uint8 [n].
  * Nearest = smallest exact squared distance in float32, lowest index among
- * equal distances.  Requires n >= 0.
+ * equal distances.  Requires 0 <= n <= 2^32 - 256 (else
+ * NSN_ERR_UNSUPPORTED).
  */
 nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table,
                                 const float* v, int64_t n, uint8_t* out,
@@ -213,6 +228,8 @@ nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table,
  *   4), and in_dtype must be NSN_F16.
  * Strides let a flush write into a preallocated cache at a group offset:
  * pass pointers advanced to the offset and the cache's sequence strides.
+ * At most 2^24 - 1 token groups (n_seq * n_tok / group_size) per call, else
+ * NSN_ERR_UNSUPPORTED (one launch covers the call).
  */
 nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype,
                         const void* x, int64_t n_seq, int64_t n_tok,
@@ -229,7 +246,8 @@ nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype,
  * x_hat_t = (H/sqrt(128)) [ s1 (s2' c(codes_t) + o'_g) ], the stored fp16
  * values taken as exact.  Layouts as nsn_quantize; output x_hat
  * [n_seq][n_tok][128] of out_dtype, sequences out_seq_stride elements apart.
- * n_tok must be a multiple of group_size.
+ * n_tok must be a multiple of group_size; at most 2^24 - 1 token groups per
+ * call, as for nsn_quantize.
  */
 nsn_status nsn_dequantize(const nsn_params* p, const uint8_t* codes,
                           int64_t codes_seq_stride, const uint16_t* meta,
@@ -284,7 +302,11 @@ typedef struct {
  *                    (NSN_DQ: uint16 [B][Hkv][cache_capacity/128][68], the
  *                    group records).
  * k_resid, v_resid   device fp16  [B][Hkv][resid_capacity][128].
- * workspace          device, >= nsn_decode_attention_workspace_size().
+ * workspace          device, >= nsn_decode_attention_workspace_size() for
+ *                    this shape.  The size is non-decreasing in n_quant_tok,
+ *                    so a workspace sized for a cache's capacity (n_quant_tok
+ *                    = cache_capacity, same batch and heads) serves every
+ *                    fill level of that cache, with or without rotary keys.
  * out      device fp32 [B][Hq][128].
  * Requires n_quant_tok + n_resid_tok >= 1.
  */

@@ -79,6 +79,9 @@ def _stride16(t):
 def _check_meta_layout(params, meta, shift):
     """Inner shapes of meta and shift for the plain and the double-quantized
     layouts (see the module doc)."""
+    import torch
+    if meta.dtype != torch.float16:
+        raise ValueError("meta must be fp16")
     if params.dq:
         if meta.dim() != 2 or meta.element_size() != 2:
             raise ValueError("with dq, meta is (n_seq, cap) of a 2-byte dtype (fp16 s2')")
@@ -87,8 +90,21 @@ def _check_meta_layout(params, meta, shift):
     else:
         if meta.dim() != 3 or meta.shape[2] != 2 or meta.element_size() != 2:
             raise ValueError("meta is (n_seq, cap, 2) fp16")
-        if shift.dim() != 3 or shift.shape[2] != 128 or shift.element_size() != 2:
+        if shift.dim() != 3 or shift.shape[2] != 128 or shift.dtype != torch.float16:
             raise ValueError("shift is (n_seq, cap // G, 128) fp16")
+
+
+def _check_extents(params, n_seq, n_tok, codes, meta, shift):
+    """Every output/input array holds n_seq sequences of n_tok tokens
+    (n_tok / G group slots for shift): the C ABI trusts these extents."""
+    for name, t in (("codes", codes), ("meta", meta), ("shift", shift)):
+        if t.shape[0] < n_seq:
+            raise ValueError(f"{name} has {t.shape[0]} sequences, fewer than {n_seq}")
+    if codes.shape[1] < n_tok or meta.shape[1] < n_tok:
+        raise ValueError("n_tok exceeds the tensors' token dimension")
+    if shift.shape[1] < n_tok // params.group_size:
+        raise ValueError(f"shift holds {shift.shape[1]} group slots, fewer than "
+                         f"n_tok // group_size = {n_tok // params.group_size}")
 
 
 def _ptr(t):
@@ -231,8 +247,9 @@ def nsn_quantize(params, x, table, codes, meta, shift, n_tok=None, stream=None):
     _check_meta_layout(params, meta, shift)
     _check_codes(params, codes)
     _check_table(params, table)
-    if x.shape[1] < n_tok or codes.shape[1] < n_tok or meta.shape[1] < n_tok:
-        raise ValueError("n_tok exceeds the tensors' token dimension")
+    if x.shape[1] < n_tok:
+        raise ValueError("n_tok exceeds the input's token dimension")
+    _check_extents(params, x.shape[0], n_tok, codes, meta, shift)
     lib = _lib.load()
     _lib.check(lib.nsn_quantize(ctypes.byref(params.c), _dtype_code(x), _ptr(x), x.shape[0], n_tok,
                                 x.stride(0), _ptr(table), _ptr(codes), codes.stride(0), _ptr(meta),
@@ -249,8 +266,9 @@ def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=No
     _check_meta_layout(params, meta, shift)
     _check_codes(params, codes)
     _check_table(params, table)
-    if codes.shape[1] < n_tok or meta.shape[1] < n_tok or out.shape[1] < n_tok:
-        raise ValueError("n_tok exceeds the tensors' token dimension")
+    if out.shape[1] < n_tok:
+        raise ValueError("n_tok exceeds the output's token dimension")
+    _check_extents(params, out.shape[0], n_tok, codes, meta, shift)
     lib = _lib.load()
     _lib.check(lib.nsn_dequantize(ctypes.byref(params.c), _ptr(codes), codes.stride(0), _ptr(meta),
                                   _stride16(meta), _ptr(shift), _stride16(shift), _ptr(table),

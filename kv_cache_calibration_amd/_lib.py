@@ -15,6 +15,7 @@ NSN_ERR_INVALID_ARG = 1
 NSN_ERR_UNSUPPORTED = 2
 NSN_ERR_WORKSPACE = 3
 NSN_ERR_HIP = 4
+NSN_ERR_INTERNAL = 5
 NSN_F16 = 0
 NSN_F32 = 1
 NSN_SCALE_ADJUST = 1

@@ -1200,6 +1200,25 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int rope, in
   *n_split = static_cast<int>((n_quant + c - 1) / c);
 }
 
+int attn_split_bound(int B, int Hq, int Hkv, int n_quant) {
+  // attn_plan's count is at most want <= min(slots / units, ceil(n /
+  // kMinChunk)) (taken at least 1), unless the chunk is capped at kMaxChunk,
+  // when it is ceil(n / kMaxChunk).  Both terms grow with n, and the plain
+  // plan has the most slots, so this bounds every plan (plain or rotary) for
+  // every count up to n_quant -- unlike the plan itself, whose rounding of
+  // the chunk to whole groups can need more partials at a smaller count.
+  if (n_quant <= 0) return 0;
+  const int grp = Hq / Hkv;
+  const int64_t units = static_cast<int64_t>(B) * Hkv * ((grp + kHB - 1) / kHB);
+  const int64_t slots = static_cast<int64_t>(kPlanCUs) * kPlanBlocksPerCU;
+  int64_t w = slots / units;
+  if (w < 1) w = 1;
+  const int64_t by_min = (n_quant + kMinChunk - 1) / kMinChunk;
+  if (w > by_min) w = by_min;
+  const int64_t by_max = (n_quant + kMaxChunk - 1) / kMaxChunk;
+  return static_cast<int>(w > by_max ? w : by_max);
+}
+
 size_t attn_workspace_bytes(int B, int Hq, int n_split) {
   return static_cast<size_t>(B) * Hq * (n_split + 1) * kPartStride * sizeof(float);
 }

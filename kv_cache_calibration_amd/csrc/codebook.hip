@@ -123,7 +123,10 @@ __global__ void prepare_kernel(const float* __restrict__ cb, int dq, uint8_t* __
   float n2 = 0.f;
 #pragma unroll
   for (int e = 0; e < M; ++e) {
-    const float c = dq ? level4(cb[k * M + e]) : cb[k * M + e];
+    // one codebook for every consumer: the entry rounded once to fp16
+    // (nearest, ties to even) or, double-quantized, to its 4-bit level (an
+    // fp16 value too); the fp32 and fp16 copies then hold the same numbers
+    const float c = dq ? level4(cb[k * M + e]) : h2f(f2h(cb[k * M + e]));
     tc[k * M + e] = c;
     th[k * M + e] = f2h(c);
     n2 = fmaf(c, c, n2);

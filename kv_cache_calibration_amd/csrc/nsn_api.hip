@@ -36,6 +36,11 @@ nsn_status hip_status(hipError_t e, const char* what) {
   return fail(NSN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// One launch covers a call: its work-items (workgroups x threads, at most
+// 256 threads per workgroup) must stay below 2^32.
+constexpr int64_t kMaxGroups = (int64_t(1) << 24) - 1;     // workgroup per token group
+constexpr int64_t kMaxNearest = (int64_t(1) << 32) - 256;  // one work-item per sub-vector
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // The shift argument: 16 bytes, or 8 with NSN_DQ (the 136-byte group records
 // are 8-byte aligned, so a cache advanced by an odd number of groups is too).
@@ -78,17 +83,20 @@ const char* nsn_status_string(nsn_status s) {
     case NSN_ERR_UNSUPPORTED: return "unsupported shape or parameter";
     case NSN_ERR_WORKSPACE: return "workspace too small";
     case NSN_ERR_HIP: return "HIP runtime error";
+    case NSN_ERR_INTERNAL: return "internal error";
   }
   return "unknown status";
 }
 
 size_t nsn_table_size(const nsn_params* p) {
-  (void)p;
+  if (check_params(p) != NSN_OK) return 0;
   return nsn::kTabBytes;
 }
 
 size_t nsn_build_codebook_workspace_size(int32_t sub_dim, int32_t n_codes, int64_t n_samples) {
-  if (n_samples < 0 || n_codes <= 0 || sub_dim <= 0) return 0;
+  if ((sub_dim != 4 && sub_dim != 8) || n_codes != 256 || n_samples < n_codes ||
+      n_samples > (int64_t(1) << 26))
+    return 0;
   return nsn::build_codebook_workspace(sub_dim, n_codes, n_samples);
 }
 
@@ -163,7 +171,8 @@ nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table, const fl
     g_err[0] = '\0';
     return NSN_OK;
   }
-  if (n > (int64_t(1) << 36)) return fail(NSN_ERR_UNSUPPORTED, "n too large");
+  if (n > kMaxNearest)
+    return fail(NSN_ERR_UNSUPPORTED, "n above %lld", static_cast<long long>(kMaxNearest));
   if (!table || !v || !out) return fail(NSN_ERR_INVALID_ARG, "table, v and out must be non-NULL");
   if (!aligned16(table) || !aligned16(v) || !aligned16(out))
     return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
@@ -223,8 +232,9 @@ nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype, const void* x, 
                   static_cast<long long>(nsub));
     NSN_TRY(check_meta_strides(p, n_tok, meta_seq_stride, shift_seq_stride));
   }
-  if (n_seq * (n_tok / G) > 0x7fffffffLL)
-    return fail(NSN_ERR_UNSUPPORTED, "too many token groups in one call");
+  if (n_seq > kMaxGroups || n_seq * (n_tok / G) > kMaxGroups)
+    return fail(NSN_ERR_UNSUPPORTED, "%lld token groups in one call (at most %lld)",
+                static_cast<long long>(n_seq * (n_tok / G)), static_cast<long long>(kMaxGroups));
   nsn::QuantArgs a{x, in_dtype == NSN_F32, n_seq, n_tok, x_seq_stride, table, codes,
                    codes_seq_stride, meta, meta_seq_stride, shift, shift_seq_stride,
                    p->sub_dim, p->group_size, static_cast<int>(p->flags & NSN_SCALE_ADJUST),
@@ -261,8 +271,9 @@ nsn_status nsn_dequantize(const nsn_params* p, const uint8_t* codes, int64_t cod
                   static_cast<long long>(nsub));
     NSN_TRY(check_meta_strides(p, n_tok, meta_seq_stride, shift_seq_stride));
   }
-  if (n_seq * (n_tok / G) > 0x7fffffffLL)
-    return fail(NSN_ERR_UNSUPPORTED, "too many token groups in one call");
+  if (n_seq > kMaxGroups || n_seq * (n_tok / G) > kMaxGroups)
+    return fail(NSN_ERR_UNSUPPORTED, "%lld token groups in one call (at most %lld)",
+                static_cast<long long>(n_seq * (n_tok / G)), static_cast<long long>(kMaxGroups));
   nsn::DequantArgs a{codes, codes_seq_stride, meta, meta_seq_stride, shift, shift_seq_stride, table,
                      n_seq, n_tok, out_dtype == NSN_F32, x_hat, out_seq_stride, p->sub_dim,
                      p->group_size, (p->flags & NSN_DQ) ? 1 : 0};
@@ -321,10 +332,8 @@ static nsn_status check_attn(const nsn_params* p, const nsn_attn_shape* s) {
 
 size_t nsn_decode_attention_workspace_size(const nsn_params* p, const nsn_attn_shape* s) {
   if (check_attn(p, s) != NSN_OK) return 0;
-  int n_split = 0, chunk = 0;
-  nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, p->group_size, 0, &n_split,
-                 &chunk);
-  return nsn::attn_workspace_bytes(s->batch, s->n_q_heads, n_split);
+  return nsn::attn_workspace_bytes(
+      s->batch, s->n_q_heads, nsn::attn_split_bound(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok));
 }
 
 static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shape* s,
@@ -350,7 +359,12 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
   int n_split = 0, chunk = 0;
   nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, p->group_size, r ? 1 : 0,
                  &n_split, &chunk);
-  const size_t need = nsn::attn_workspace_bytes(s->batch, s->n_q_heads, n_split);
+  // the size query's monotone bound, so one workspace sized for a cache
+  // serves every fill level of it
+  const size_t need = nsn::attn_workspace_bytes(
+      s->batch, s->n_q_heads, nsn::attn_split_bound(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok));
+  if (n_split > nsn::attn_split_bound(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok))
+    return fail(NSN_ERR_INTERNAL, "split plan above its bound");
   if (workspace_bytes < need)
     return fail(NSN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   nsn::AttnArgs a{};

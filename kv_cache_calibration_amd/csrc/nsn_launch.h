@@ -90,6 +90,10 @@ struct AttnArgs {
 // more workspace than the plain plan the size query reports.
 void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int rope,
                int* n_split, int* chunk);
+// Upper bound of the split count over both plans and every quantized-token
+// count in [0, n_quant]; non-decreasing in n_quant.  The workspace size the
+// library asks for and checks.
+int attn_split_bound(int B, int Hq, int Hkv, int n_quant);
 size_t attn_workspace_bytes(int B, int Hq, int n_split);
 hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s);
 

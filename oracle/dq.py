@@ -19,8 +19,10 @@ The pages give neither the grids nor the second-level scales.  Readings:
     clamped to [-7, 7], stored as code + 8 (1..15; 0 when the scale is 0);
     decoded o' = (code - 8) * scale.
   * s2' keeps fp16 (the pages name only o and s1).
-  * The decisions (codes) are taken in float32, as the GPU takes them, from
-    the float32 value of the fp64 quantity.
+  * The decisions (codes) are the reading's definitions evaluated exactly
+    (float64) on the unrounded s1 and o' and the stored fp16 lo, hi and
+    scale; an implementation that divides in lower precision can land on
+    the other side of an exact half step only within its rounding error.
   * Record per group (little-endian): fp16 lo, fp16 hi, fp16 scale, 2 zero
     bytes; 64 bytes of o' codes (channel c in byte c // 2, low nibble for
     even c); G / 2 bytes of s1 codes (token t of the group likewise).
@@ -70,17 +72,16 @@ def dq_encode_group(s1, o_rot):
     s1 = np.asarray(s1, np.float64)
     o_rot = np.asarray(o_rot, np.float64)
     lo16, hi16 = np.float16(s1.min()), np.float16(s1.max())
-    lo, hi = np.float32(lo16), np.float32(hi16)
+    lo, hi = np.float64(lo16), np.float64(hi16)
     if hi > lo:
-        inv = np.float32(15.0) / (hi - lo)
-        t = (s1.astype(np.float32) - lo) * inv
+        t = (s1 - lo) * 15.0 / (hi - lo)
         c1 = np.clip(np.rint(t).astype(np.int64), 0, 15)
     else:
         c1 = np.zeros(s1.size, np.int64)
     sc16 = np.float16(np.abs(o_rot).max() / 7.0)
-    sc = np.float32(sc16)
+    sc = np.float64(sc16)
     if sc > 0:
-        t = o_rot.astype(np.float32) / sc
+        t = o_rot / sc
         co = np.clip(np.rint(t).astype(np.int64), -7, 7) + 8
     else:
         co = np.zeros(o_rot.size, np.int64)

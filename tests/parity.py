@@ -12,7 +12,9 @@ Reconstruction: the GPU's dequantization of its own bytes matches the
 oracle's dequantization of the same bytes to 1e-5 relative L2 (fp32
 output); against the oracle's own reconstruction, 1e-3 relative L2.
 
-Attention: max-abs 2e-3 against the oracle on the same cache bytes.
+Attention: on the same cache bytes, max-abs 2e-3 against the oracle and,
+per (batch, q head), relative L2 1e-4 (the codes are shared, so only the
+fp32 accumulation differs; 2e-3 alone would let a dropped token group pass).
 """
 
 import numpy as np
@@ -23,6 +25,7 @@ TIE_REL = 1e-5
 RECON_REL = 1e-3
 SAME_BYTES_REL = 1e-5
 ATTN_ABS = 2e-3
+ATTN_REL = 1e-4
 
 
 def ulp16(v):
@@ -69,7 +72,15 @@ def _nibbles(b, n):
     return out[:n]
 
 
-DQ_TIE = 1e-3   # distance of the oracle's fp32 grid coordinate from a half step
+# Double-quantized codes: the oracle decides them exactly (float64); the GPU
+# divides in float32 from its own float32 s1 and o'.  A code may differ by one
+# only where the exact grid coordinate t lies within the GPU's rounding error
+# of a half step: DQ_TIE grid steps for o' (t = o'/sc, the float32 mean is
+# good to ~1e-6 absolute and sc >= 1e-3 on these inputs), plus, for s1
+# (t = (s1 - lo) * 15 / (hi - lo)), the float32 s1's relative error S1_REL
+# scaled by 15 * s1 / (hi - lo).
+DQ_TIE = 1e-3
+S1_REL = 4e-6
 
 
 def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128):
@@ -96,7 +107,7 @@ def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128):
         s1x = it["s1"][g * G:(g + 1) * G]
         ox = it["o_rot"][g]
         if np.array_equal(recs_g[g, :8], recs_o[g, :8]):
-            lo, hi, sc = (np.float32(v) for v in ho)
+            lo, hi, sc = (float(v) for v in ho)
             for part, n, exact, ref in (("o", d, ox, None), ("s1", G, s1x, None)):
                 off = 8 if part == "o" else 8 + d // 2
                 cg = _nibbles(recs_g[g, off:off + n // 2], n)
@@ -105,11 +116,12 @@ def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128):
                 if diff.size == 0:
                     continue
                 if part == "o":
-                    t = exact.astype(np.float32) / sc
+                    t = exact / sc
+                    win = DQ_TIE
                 else:
-                    t = (exact.astype(np.float32) - lo) * (np.float32(15) / (hi - lo))
-                t = t.astype(np.float64)
-                near = np.abs(t - np.floor(t) - 0.5) < DQ_TIE
+                    t = (exact - lo) * 15.0 / (hi - lo)
+                    win = DQ_TIE + 15.0 * S1_REL * max(abs(lo), abs(hi)) / (hi - lo)
+                near = np.abs(t - np.floor(t) - 0.5) < win
                 assert np.all(near[diff]) and np.all(np.abs(cg[diff] - co[diff]) == 1), (
                     f"group {g} {part} codes differ away from a half step at {diff[:5]}")
                 n_near += diff.size
@@ -148,3 +160,25 @@ def rel_l2(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_attention(got, want, what=""):
+    """Attention output `got` against the oracle's `want` (same shape, last
+    axis the 128 channels): max-abs <= ATTN_ABS over all entries and relative
+    L2 <= ATTN_REL for every (batch, q head) row.  Rows where the oracle is
+    not finite (heads it was not asked for) are skipped.  Prints and returns
+    (max-abs, worst per-row relative L2)."""
+    g = np.asarray(got, np.float64).reshape(-1, np.shape(got)[-1])
+    w = np.asarray(want, np.float64).reshape(-1, np.shape(want)[-1])
+    keep = np.isfinite(w).all(axis=1)
+    assert keep.any(), "no oracle rows to compare"
+    g, w = g[keep], w[keep]
+    assert np.isfinite(g).all(), "non-finite attention output"
+    err = float(np.abs(g - w).max())
+    rel = np.linalg.norm(g - w, axis=1) / np.maximum(np.linalg.norm(w, axis=1), 1e-30)
+    worst = float(rel.max())
+    print(f"  {what} attention: max-abs {err:.2e}, worst per-head rel-L2 {worst:.2e} "
+          f"over {w.shape[0]} heads", flush=True)
+    assert err <= ATTN_ABS, f"max-abs {err:.3e} > {ATTN_ABS}"
+    assert worst <= ATTN_REL, f"per-head rel-L2 {worst:.3e} > {ATTN_REL} (row {int(rel.argmax())})"
+    return err, worst

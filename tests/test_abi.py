@@ -47,8 +47,8 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.nsn_version().decode().startswith("nsnq")
-    for s in range(5):
-        assert lib.nsn_status_string(s)
+    for s in range(6):
+        assert lib.nsn_status_string(s) not in (b"", b"unknown status")
     assert lib.nsn_status_string(99) == b"unknown status"
 
 
@@ -186,6 +186,27 @@ def test_attention_workspace_size_and_check(lib):
     assert st == _lib.NSN_ERR_WORKSPACE
     st = lib.nsn_decode_attention(P(), ctypes.byref(s), *args, NULL, need, FAKE, NULL)
     assert st == _lib.NSN_ERR_INVALID_ARG
+
+
+def test_attention_workspace_covers_every_fill_level(lib):
+    """One size query at a cache's capacity covers every smaller n_quant_tok
+    (the split plan rounds chunks to whole groups, so its own count is not
+    monotone in the token count); checked on shapes where it was not."""
+    for B, Hq, Hkv, G, cap in [(1, 32, 8, 128, 65536), (2, 8, 2, 128, 131072), (1, 4, 1, 256, 32768),
+                               (16, 32, 8, 128, 32768), (3, 12, 4, 128, 8192)]:
+        def size(n):
+            s = _lib.nsn_attn_shape(B, Hq, Hkv, n, 1, cap, 1, 0.088)
+            return lib.nsn_decode_attention_workspace_size(P(G=G), ctypes.byref(s))
+        sizes = [size(n) for n in range(0, cap + 1, G)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), (B, Hq, Hkv, G)
+        full = sizes[-1]
+        args = [FAKE] * 10
+        for n in range(G, cap + 1, G):
+            s = _lib.nsn_attn_shape(B, Hq, Hkv, n, 1, cap, 1, 0.088)
+            # one byte short of the query's answer at n: rejected before any launch
+            st = lib.nsn_decode_attention(P(G=G), ctypes.byref(s), *args, FAKE, size(n) - 1, FAKE, NULL)
+            assert st == _lib.NSN_ERR_WORKSPACE
+            assert size(n) <= full
 
 
 @pytest.mark.parametrize("q_pos,base,status", [
@@ -343,3 +364,72 @@ def test_binding_rejects_wrong_dtypes_and_sizes():
         nsnq._check_attention_shapes(p, q, plain, plain, kr, kr, out.half())
     with pytest.raises(ValueError):
         nsnq._check_attention_shapes(p, q, plain, plain, kr.float(), kr, out)
+
+
+def test_binding_checks_sequence_and_group_extents():
+    """The C ABI trusts the sequence count and the group slots it is given:
+    the binding rejects codes, meta or shift tensors with fewer sequences
+    than the input, a shift view ending before the last group, and a
+    non-fp16 meta or shift (host tensors; the checks run before any call)."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    p = nsnq.Params(sub_dim=4, group_size=128)
+    n_seq, T = 3, 512
+    codes = torch.zeros((n_seq, T, 32), dtype=torch.uint8)
+    meta = torch.zeros((n_seq, T, 2), dtype=torch.float16)
+    shift = torch.zeros((n_seq, T // 128, 128), dtype=torch.float16)
+    nsnq._check_extents(p, n_seq, T, codes, meta, shift)
+    nsnq._check_extents(p, n_seq, T - 128, codes, meta, shift[:, :3])
+    for args in ((codes[:2], meta, shift), (codes, meta[:2], shift), (codes, meta, shift[:1]),
+                 (codes, meta, shift[:, :3]), (codes[:, :384], meta, shift), (codes, meta[:, :500], shift)):
+        with pytest.raises(ValueError):
+            nsnq._check_extents(p, n_seq, T, *args)
+    with pytest.raises(ValueError):
+        nsnq._check_meta_layout(p, meta.view(torch.int16), shift)
+    with pytest.raises(ValueError):
+        nsnq._check_meta_layout(p, meta, shift.view(torch.bfloat16))
+
+
+def test_launch_size_limits_are_rejected_up_front(lib):
+    """A call whose single launch would need 2^32 or more work-items is
+    refused with NSN_ERR_UNSUPPORTED before any HIP call (fake pointers,
+    nothing launched); one group below the limit passes validation (checked
+    on the error path only: a too-small stride makes it fail afterwards)."""
+    G = 128
+    limit = (1 << 24) - 1
+    # n_seq = 1: no strides checked, so the group count decides
+    st = _q(lib, P(), n_seq=1, n_tok=(limit + 1) * G, xs=0, cs=0, ms=0, ss=0)
+    assert st == _lib.NSN_ERR_UNSUPPORTED
+    assert b"token groups" in lib.nsn_last_error()
+    st = lib.nsn_dequantize(P(), FAKE, 0, FAKE, 0, FAKE, 0, FAKE, 1, (limit + 1) * G, 0, FAKE, 0, NULL)
+    assert st == _lib.NSN_ERR_UNSUPPORTED
+    # strides are checked before the count: a short stride still reports
+    # INVALID_ARG at a count within the limit (nothing is launched)
+    st = _q(lib, P(), n_seq=2, n_tok=(limit // 2) * G, xs=100)
+    assert st == _lib.NSN_ERR_INVALID_ARG
+    st = lib.nsn_nearest_codeword(P(), FAKE, FAKE, (1 << 32) - 255, FAKE, NULL)
+    assert st == _lib.NSN_ERR_UNSUPPORTED
+
+
+def _no_hip_device():
+    torch = pytest.importorskip("torch")
+    return torch.cuda.device_count() == 0
+
+
+def test_failed_launch_reports_nsn_err_hip(lib):
+    """A launch that the HIP runtime refuses comes back as NSN_ERR_HIP with
+    the runtime's message.  Forced from the host: with no HIP device visible
+    every launch fails, so valid arguments (fake device pointers, never
+    dereferenced) reach the launch and fail there.  Skipped where a device
+    exists, since there the launch would run on the fake pointers."""
+    if not _no_hip_device():
+        pytest.skip("a HIP device is visible: a launch on fake pointers would run")
+    st = _q(lib, P(), n_seq=1, n_tok=128, xs=0, cs=0, ms=0, ss=0)
+    assert st == _lib.NSN_ERR_HIP
+    msg = lib.nsn_last_error().decode()
+    assert msg.startswith("nsn_quantize launch:") and len(msg) > len("nsn_quantize launch: ")
+    st = lib.nsn_residual_append(FAKE, 1, FAKE, 0, 4, 0, NULL)
+    assert st == _lib.NSN_ERR_HIP
+    # a later successful call clears the detail string
+    assert _q(lib, P(), n_seq=0) == _lib.NSN_OK
+    assert lib.nsn_last_error() == b""

@@ -1,5 +1,6 @@
 """Parity of nsn_decode_attention (HIP, through the C ABI) with the oracle on
-the same cache bytes: max-abs error <= 2e-3 (the output is fp32)."""
+the same cache bytes: max-abs error <= 2e-3 and per-head relative L2 <= 1e-4
+(the output is fp32)."""
 
 import math
 
@@ -9,7 +10,7 @@ import pytest
 import oracle
 import synth
 from tests.gpu_common import DEV, alloc_outputs, requires_gpu, table_for, torch
-from tests.parity import ATTN_ABS, rel_l2
+from tests.parity import check_attention
 
 import kv_cache_calibration_amd as nsnq
 
@@ -70,10 +71,7 @@ def check(cache, q, heads=None, scale=None):
     k, v, kr, vr = to_np(cache)
     want = oracle.decode_attention(q.cpu().numpy(), k, v, kr, vr, cache["C"], cache["G"],
                                    cache["Nq"], cache["R"], scale, heads=heads)
-    sel = np.isfinite(want)
-    err = np.abs(got[sel] - want[sel]).max()
-    assert err <= ATTN_ABS, err
-    assert rel_l2(got[sel], want[sel]) < 2e-3
+    err, _ = check_attention(got, want)
     return err
 
 
@@ -111,8 +109,7 @@ def test_attention_zero_query_is_mean_of_values():
     vals = np.concatenate([oracle.dequantize(*(a[0, 0, :512] for a in v[:2]), v[2][0, 0, :4],
                                              cache["C"], 128),
                            vr[0, 0, :3].astype(np.float64)])
-    for h in range(4):
-        assert np.abs(got[0, h] - vals.mean(0)).max() <= ATTN_ABS
+    check_attention(got[0], np.broadcast_to(vals.mean(0), got[0].shape), "q = 0")
 
 
 def test_attention_large_scale_softmax_is_stable():
@@ -144,8 +141,7 @@ def test_attention_decode_workload_sampled():
         v = tuple(sl(t) for t in cache["v"])
         want = oracle.decode_attention(qn[b:b + 1, h:h + 1], k, v, sl(cache["kr"]), sl(cache["vr"]),
                                        cache["C"], w["G"], w["Nq"], w["R"], 1 / math.sqrt(128))
-        err = np.abs(got[b, h] - want[0, 0]).max()
-        assert err <= ATTN_ABS, (b, h, err)
+        check_attention(got[b, h], want[0, 0], f"(b={b}, h={h})")
 
 
 @pytest.mark.parametrize("m,G", [(4, 128), (8, 256)])
@@ -170,7 +166,7 @@ def test_attention_largest_chunk_sampled(m, G):
         v = tuple(sl(t) for t in cache["v"])
         want = oracle.decode_attention(qn[b:b + 1, h:h + 1], k, v, sl(cache["kr"]), sl(cache["vr"]),
                                        cache["C"], G, Nq, R, scale)
-        assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
+        check_attention(got[b, h], want[0, 0], f"(b={b}, h={h})")
 
 
 @pytest.mark.parametrize("m,G", [(4, 128), (8, 256)])

@@ -13,7 +13,7 @@ import oracle
 import synth
 from tests.gpu_common import DEV, requires_gpu, torch
 from tests.golden import load_codebook
-from tests.parity import ATTN_ABS, SAME_BYTES_REL, check_dq_sequence, rel_l2
+from tests.parity import SAME_BYTES_REL, check_attention, check_dq_sequence, rel_l2
 
 import kv_cache_calibration_amd as nsnq
 
@@ -228,9 +228,7 @@ def test_attention_dq_parity(B, Hq, Hkv, Nq, R, m):
     v = _decoded(cache["v"], B, Hkv)
     want = oracle.decode_attention(q.cpu().numpy(), k, v, cache["kr"].cpu().numpy(),
                                    cache["vr"].cpu().numpy(), cache["C4"], G, Nq, R, scale)
-    err = np.abs(got - want).max()
-    assert err <= ATTN_ABS, err
-    assert rel_l2(got, want) < 2e-3
+    check_attention(got, want, "DQ")
 
 
 def test_attention_dq_decode_workload_sampled():
@@ -270,7 +268,7 @@ def test_attention_dq_decode_workload_sampled():
                                        cache["kr"][b:b + 1, kvh:kvh + 1].cpu().numpy(),
                                        cache["vr"][b:b + 1, kvh:kvh + 1].cpu().numpy(), C4, G, Nq, R,
                                        scale)
-        assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
+        check_attention(got[b, h], want[0, 0], f"DQ (b={b}, h={h})")
 
 
 def test_attention_dq_largest_chunk_sampled():
@@ -311,7 +309,7 @@ def test_attention_dq_largest_chunk_sampled():
                                        cache["kr"][b:b + 1, kvh:kvh + 1].cpu().numpy(),
                                        cache["vr"][b:b + 1, kvh:kvh + 1].cpu().numpy(), C4, G, Nq, R,
                                        scale)
-        assert np.abs(got[b, h] - want[0, 0]).max() <= ATTN_ABS, (b, h)
+        check_attention(got[b, h], want[0, 0], f"DQ (b={b}, h={h})")
 
 
 def run_dq_attention_rope(cache, q, scale, q_pos, base):
@@ -349,9 +347,7 @@ def test_attention_dq_rope_parity(B, Hq, Hkv, Nq, R, m, dpos, base):
     want = oracle.decode_attention_rope(q.cpu().numpy(), k, v, cache["kr"].cpu().numpy(),
                                         cache["vr"].cpu().numpy(), cache["C4"], G, Nq, R, scale,
                                         q_pos, base)
-    err = np.abs(got - want).max()
-    assert err <= ATTN_ABS, err
-    assert rel_l2(got, want) < 2e-3
+    check_attention(got, want, "DQ rotary")
 
 
 @pytest.mark.parametrize("rope", [False, True])
@@ -384,4 +380,4 @@ def test_attention_dq_partly_filled_cache_and_residual(rope):
         got = run_dq_attention(cache, q, scale)
         want = oracle.decode_attention(q.cpu().numpy(), k, v, kr, vr, cache["C4"], G, Nq, R, scale)
     assert np.isfinite(got).all()
-    assert np.abs(got - want).max() <= ATTN_ABS
+    check_attention(got, want, f"DQ partly filled rope={rope}")

@@ -15,7 +15,7 @@ import oracle
 import synth
 from tests.gpu_common import DEV, requires_gpu, torch
 from tests.golden import load_codebook
-from tests.parity import ATTN_ABS
+from tests.parity import check_attention
 
 import kv_cache_calibration_amd as nsnq
 
@@ -90,7 +90,7 @@ def test_decode_loop(dq, rope):
                                                     scale, nq + nr - 1, 10000.0)
             else:
                 want = oracle.decode_attention(q.cpu().numpy(), k, v, krn, vrn, Cref, G, nq, nr, scale)
-            assert np.abs(out.cpu().numpy() - want).max() <= ATTN_ABS, step
+            check_attention(out.cpu().numpy(), want, f"decode loop step {step}")
     # the flushed cache equals one quantize call over the same tokens
     kc2 = tuple(torch.zeros(s, dtype=d, device=DEV) for s, d in nsnq.cache_layout(p, n_seq, nq))
     nsnq.nsn_quantize(p, K[:, :nq], t, *kc2)

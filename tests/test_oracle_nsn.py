@@ -141,8 +141,23 @@ def test_nsn_plus_hadamard_output_approaches_standard_normal():
                          for s in range(16)])
     # pooled second moment is exactly one: every token has norm sqrt(d)
     assert abs((hk ** 2).mean() - 1.0) < 1e-12
+    # x5 outlier noise: the looser bounds are a property of that model, not
+    # of sampling.  With offsets of ~20 on the outlier channels, s1 depends on
+    # the sign of their x5 noise, so after Normalize #1 a token's outlier
+    # channels are correlated and each rotated channel's variance depends on
+    # its sign pattern over the sequence's 4 outlier channels (measured 0.106
+    # at 16 sequences, 0.051 at 64: it averages out over sequences); and
+    # Normalize #2, dominated by 4 channels of variance 25, is a heavy scale
+    # mixture (excess kurtosis 0.24 at 16 sequences, 0.20 at 64).
     mu, dv, sk, ku = _moments(hk)
     assert mu < 0.03 and dv < 0.12 and sk < 0.06 and ku < 0.35, (mu, dv, sk, ku)
+    # without the x5 noise (the tiny workload's model) the keys meet the
+    # tighter bounds 0.05 (variance), 0.05 (skew), 0.15 (excess kurtosis)
+    K1, _ = synth.kv_numpy(16, 4096, 1.0, seed=11)
+    h1 = np.concatenate([oracle.rotate(oracle.nsn(K1[s].astype(np.float64), 128)[0])
+                         for s in range(16)])
+    mu, dv, sk, ku = _moments(h1)
+    assert mu < 0.02 and dv < 0.05 and sk < 0.05 and ku < 0.15, (mu, dv, sk, ku)
     mu, dv, sk, ku = _moments(hv)
     assert mu < 0.03 and dv < 0.05 and sk < 0.05 and ku < 0.1, (mu, dv, sk, ku)
     # the raw keys fail every one of these bounds
