@@ -28,8 +28,10 @@
  *  - Inputs must be finite.  Non-finite inputs give unspecified output but
  *    never an out-of-bounds access.
  *  - The library keeps no mutable global state besides the thread-local
- *    error string; calls on different streams may run concurrently as long
- *    as their output buffers do not overlap.
+ *    error string and the static device scratch of
+ *    nsn_decode_attention_noalloc; calls on different streams may run
+ *    concurrently as long as their output buffers do not overlap (and, for
+ *    nsn_decode_attention_noalloc, not on the same GPU at all).
  */
 #ifndef NSN_H
 #define NSN_H
@@ -354,6 +356,32 @@ nsn_status nsn_decode_attention_rope(const nsn_params* p, const nsn_attn_shape* 
                                      const uint16_t* k_resid, const uint16_t* v_resid,
                                      const void* table, void* workspace, size_t workspace_bytes,
                                      float* out, void* stream);
+
+/*
+ * nsn_decode_attention_noalloc -- nsn_decode_attention without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The split partials go to a static device array of the library, 4 MiB
+ * (4194304 bytes) per GPU, held from the first call on that GPU until the
+ * process ends.  Shapes whose nsn_decode_attention_workspace_size() exceeds
+ * that return NSN_ERR_UNSUPPORTED (use nsn_decode_attention); the decode
+ * workload B = 16, 32 q heads on 8 kv heads needs 1.9 MB at any cache
+ * length.  Nothing is allocated or freed, by the library or any library it
+ * calls.  Every call on one GPU shares that GPU's array (nothing in it needs
+ * to start at zero: every partial is written before it is read), so calls
+ * that overlap on one GPU -- on different streams, or from different
+ * threads -- race and must be serialized by the caller.  Arguments, layouts,
+ * results and errors are otherwise those of nsn_decode_attention, and the
+ * output equals its output for the same inputs.
+ */
+nsn_status nsn_decode_attention_noalloc(const nsn_params* p, const nsn_attn_shape* s,
+                                        const uint16_t* q, const uint8_t* k_codes,
+                                        const uint16_t* k_meta, const uint16_t* k_shift,
+                                        const uint8_t* v_codes, const uint16_t* v_meta,
+                                        const uint16_t* v_shift, const uint16_t* k_resid,
+                                        const uint16_t* v_resid, const void* table,
+                                        float* out, void* stream);
 
 /* Static description of a status code. */
 const char* nsn_status_string(nsn_status s);

@@ -37,6 +37,7 @@ __all__ = [
     "nsn_residual_append",
     "nsn_decode_attention",
     "nsn_decode_attention_rope",
+    "nsn_decode_attention_noalloc",
     "nsn_decode_attention_workspace_size",
     "lib_path",
     "cache_layout",
@@ -326,6 +327,14 @@ def nsn_decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, w
                       n_quant_tok, n_resid_tok, softmax_scale, stream, None)
 
 
+def nsn_decode_attention_noalloc(params, q, k_cache, v_cache, k_resid, v_resid, table, out,
+                                 n_quant_tok, n_resid_tok, softmax_scale, stream=None):
+    """nsn_decode_attention without a workspace: the library's static device
+    scratch holds the split partials (calls on one GPU must not overlap)."""
+    _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, None, out,
+                      n_quant_tok, n_resid_tok, softmax_scale, stream, None, noalloc=True)
+
+
 def _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out):
     """The sizes the C ABI derives from the shape struct must match the
     tensors: q and out (B, Hq, 128), codes (B, Hkv, cap, 128 // m), meta
@@ -359,7 +368,7 @@ def _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out):
 
 
 def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
-                      n_quant_tok, n_resid_tok, softmax_scale, stream, rope):
+                      n_quant_tok, n_resid_tok, softmax_scale, stream, rope, noalloc=False):
     kc, km, ks = k_cache
     vc, vm, vs = v_cache
     _dev(q, kc, km, ks, vc, vm, vs, k_resid, v_resid, table, workspace, out)
@@ -372,6 +381,11 @@ def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, work
     _check_table(params, table)
     s = _shape(B, Hq, Hkv, n_quant_tok, n_resid_tok, cap, k_resid.shape[2], softmax_scale)
     lib = _lib.load()
+    if noalloc:
+        _lib.check(lib.nsn_decode_attention_noalloc(
+            ctypes.byref(params.c), ctypes.byref(s), _ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc),
+            _ptr(vm), _ptr(vs), _ptr(k_resid), _ptr(v_resid), _ptr(table), _ptr(out), _stream(stream)))
+        return
     bufs = (_ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc), _ptr(vm), _ptr(vs), _ptr(k_resid),
             _ptr(v_resid), _ptr(table), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))

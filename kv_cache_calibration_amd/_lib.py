@@ -76,6 +76,8 @@ SIGNATURES = {
                                                   ctypes.POINTER(nsn_attn_shape)]),
     "nsn_decode_attention": (_ST, [ctypes.POINTER(nsn_params), ctypes.POINTER(nsn_attn_shape),
                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "nsn_decode_attention_noalloc": (_ST, [ctypes.POINTER(nsn_params), ctypes.POINTER(nsn_attn_shape),
+                                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "nsn_decode_attention_rope": (_ST, [ctypes.POINTER(nsn_params), ctypes.POINTER(nsn_attn_shape),
                                         ctypes.POINTER(nsn_rope), _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _P, _SZ, _P, _P]),

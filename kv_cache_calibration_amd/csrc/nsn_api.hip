@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include <cmath>
+#include <mutex>
 
 #include "nsn.h"
 #include "nsn_device.h"
@@ -84,6 +85,7 @@ const char* nsn_status_string(nsn_status s) {
     case NSN_ERR_WORKSPACE: return "workspace too small";
     case NSN_ERR_HIP: return "HIP runtime error";
     case NSN_ERR_INTERNAL: return "internal error";
+    default: break;
   }
   return "unknown status";
 }
@@ -336,6 +338,33 @@ size_t nsn_decode_attention_workspace_size(const nsn_params* p, const nsn_attn_s
       s->batch, s->n_q_heads, nsn::attn_split_bound(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok));
 }
 
+// Scratch of nsn_decode_attention_noalloc: the split partials live in a
+// static device array instead of a caller workspace.  In host code `scratch`
+// names a host-side stand-in, so its device address is looked up once per
+// device (with that device current) and only that address is used.
+namespace {
+constexpr size_t kScratchBytes = size_t(4) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+}  // namespace
+
 static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shape* s,
                                         const nsn_rope* r, const uint16_t* q,
                                         const uint8_t* k_codes, const uint16_t* k_meta,
@@ -343,15 +372,17 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
                                         const uint16_t* v_meta, const uint16_t* v_shift,
                                         const uint16_t* k_resid, const uint16_t* v_resid,
                                         const void* table, void* workspace, size_t workspace_bytes,
-                                        float* out, void* stream, const char* what) {
+                                        float* out, void* stream, const char* what,
+                                        bool use_scratch = false) {
   NSN_TRY(check_attn(p, s));
-  if (!q || !table || !workspace || !out)
+  if (!q || !table || (!workspace && !use_scratch) || !out)
     return fail(NSN_ERR_INVALID_ARG, "q, table, workspace and out must be non-NULL");
   if (s->n_quant_tok > 0 && (!k_codes || !k_meta || !k_shift || !v_codes || !v_meta || !v_shift))
     return fail(NSN_ERR_INVALID_ARG, "cache arrays must be non-NULL when n_quant_tok > 0");
   if (s->n_resid_tok > 0 && (!k_resid || !v_resid))
     return fail(NSN_ERR_INVALID_ARG, "residual arrays must be non-NULL when n_resid_tok > 0");
   const void* ptrs[] = {q, k_codes, k_meta, v_codes, v_meta, k_resid, v_resid, table, workspace, out};
+  // (workspace is NULL on the no-allocation path: skipped here)
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   if ((k_shift && !shift_aligned(p, k_shift)) || (v_shift && !shift_aligned(p, v_shift)))
@@ -365,8 +396,17 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
       s->batch, s->n_q_heads, nsn::attn_split_bound(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok));
   if (n_split > nsn::attn_split_bound(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok))
     return fail(NSN_ERR_INTERNAL, "split plan above its bound");
+  if (use_scratch && need > kScratchBytes)
+    return fail(NSN_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of split partials, above the %zu bytes of static "
+                "scratch of nsn_decode_attention_noalloc (use nsn_decode_attention)",
+                need, kScratchBytes);
   if (workspace_bytes < need)
     return fail(NSN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (use_scratch) {
+    const hipError_t e = scratch_of_current_device(&workspace);
+    if (e != hipSuccess) return hip_status(e, "nsn_decode_attention_noalloc scratch lookup");
+  }
   nsn::AttnArgs a{};
   a.B = s->batch;
   a.Hq = s->n_q_heads;
@@ -408,6 +448,18 @@ nsn_status nsn_decode_attention(const nsn_params* p, const nsn_attn_shape* s, co
   return decode_attention_impl(p, s, nullptr, q, k_codes, k_meta, k_shift, v_codes, v_meta, v_shift,
                                k_resid, v_resid, table, workspace, workspace_bytes, out, stream,
                                "nsn_decode_attention launch");
+}
+
+nsn_status nsn_decode_attention_noalloc(const nsn_params* p, const nsn_attn_shape* s,
+                                        const uint16_t* q, const uint8_t* k_codes,
+                                        const uint16_t* k_meta, const uint16_t* k_shift,
+                                        const uint8_t* v_codes, const uint16_t* v_meta,
+                                        const uint16_t* v_shift, const uint16_t* k_resid,
+                                        const uint16_t* v_resid, const void* table, float* out,
+                                        void* stream) {
+  return decode_attention_impl(p, s, nullptr, q, k_codes, k_meta, k_shift, v_codes, v_meta, v_shift,
+                               k_resid, v_resid, table, nullptr, kScratchBytes, out, stream,
+                               "nsn_decode_attention_noalloc launch", true);
 }
 
 nsn_status nsn_decode_attention_rope(const nsn_params* p, const nsn_attn_shape* s,
