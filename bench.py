@@ -142,7 +142,8 @@ def main():
     n_seq_t = per_layer * L                  # sequences per tensor
     T = w4["T"]
     n_seq = 2 * n_seq_t                      # K and V in one launch
-    cap = T + G                              # room for one streamed group
+    n_flush = 4                              # streaming phase: 512 appends, 4 flushes
+    cap = T + n_flush * G                    # room for the streamed groups
     x = torch.empty((n_seq, T, D), dtype=torch.float16, device=dev)
     for layer in range(L):
         a, b = layer * per_layer, (layer + 1) * per_layer
@@ -363,6 +364,43 @@ def main():
     ms_attn_dq_rope = side_ms(evadr)
     del cachesq
 
+    # side measurement, outside the step: the prefill workload's streaming
+    # phase at full size -- 512 decode steps, each appending one token per
+    # sequence (2048 sequences, K and V) to the residual window, the window
+    # flushed into the cache behind the prefill every 128 steps (4 flushes)
+    n_app = n_flush * G
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evf = []
+    ea.record(stream)
+    for t in range(n_app):
+        nsnq.nsn_residual_append(newtok[t % G], resid, t % G)
+        if (t + 1) % G == 0:
+            off = T + (t // G) * G
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            nsnq.nsn_quantize(p, resid, table, codes[:, off:], meta[:, off:], shift[:, off // G:])
+            b.record(stream)
+            evf.append((a, b))
+    eb.record(stream)
+    torch.cuda.synchronize()
+    stream_ms = ea.elapsed_time(eb)
+    flush_ms = [a.elapsed_time(b) for a, b in evf]
+    streaming = {
+        "appends": n_app, "flushes": n_flush, "sequences": n_seq,
+        "phase_ms": stream_ms,
+        "per_append_us": (stream_ms - sum(flush_ms)) * 1e3 / n_app,
+        "flush_ms": flush_ms,
+        "decode_positions_per_s": n_app / (stream_ms * 1e-3),
+        "bytes": n_app * n_seq * D * 2 * 2 + n_flush * quant_bytes(n_seq, G, m, G),
+        "note": "launch-bound (one append launch per position): not a roofline measurement",
+    }
+    streaming["gbps"] = streaming["bytes"] / (stream_ms * 1e-3) / 1e9
+    log(f"streaming phase: {n_app} appends + {n_flush} flushes in {stream_ms:.2f} ms")
+
+    # side measurements, outside the step: the three small workloads, each
+    # exactly as stated (launch-bound, reported for completeness)
+    small = small_workloads(nsnq, synth, table, table1, cb, dev, stream)
+
     qb = quant_bytes(n_seq, T, m, G)
     ab = attn_bytes(B3, Hq, Hkv, Nq, R, m, G)
     app_b = G * n_seq * D * 2 * 2
@@ -390,6 +428,9 @@ def main():
         "attention_dq_rope_ms": ms_attn_dq_rope,
         "flush_gbps": fb / (ms["flush"] * 1e-3) / 1e9,
         "dequantize_gbps": db / (ms["dequantize"] * 1e-3) / 1e9,
+        # sequence positions of the prefill (batch 4 x 131072) per second:
+        # every position is 32 layers x 8 kv heads x (K, V) token-heads
+        "prefill_positions_per_s": w4["B"] * T / (ms["quantize"] * 1e-3) * (32 / L),
     }
     rates["quantize_frac_hbm"] = rates["quantize_gbps"] / HBM_PEAK_GBPS
     rates["attention_frac_hbm"] = rates["attention_gbps"] / HBM_PEAK_GBPS
@@ -423,7 +464,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x, caches[0], G, m, cb.cpu().numpy(), qb, ab, R, Nq, scale, step_bytes)
+        cpu = cpu_baseline(x, caches[0], G, m, cb.cpu().numpy(), cb1.cpu().numpy(), qb, ab, R, Nq,
+                           scale, step_bytes, n_seq, synth)
 
     line = {
         "metric": "KV quantize GB/s (fp16 in) + quantized decode-attn GB/s, % of HBM roofline",
@@ -453,6 +495,8 @@ def main():
         "codebook_tune_ms": tune_ms,
         "codebook_tune_iters": TUNE_ITERS,
         "roofline": roofline,
+        "streaming": streaming,
+        "small_workloads": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -502,8 +546,71 @@ def measured_traffic(src_path, algorithmic_bytes):
         return None
 
 
-def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
-    """Time the oracle on a bounded sample of the same workload."""
+def small_workloads(nsnq, synth, table2, table1, cb2, dev, stream):
+    """Quantize (+ dequantize) of the tiny, 2-bit layer and 1-bit layer
+    workloads at their stated sizes: median of 20 launches each.  These are
+    too small to fill the chip or to leave the caches (the tiny one is two
+    workgroups) and take microseconds, so launch latency dominates: reported
+    for completeness, not as roofline measurements."""
+    import numpy as np
+    import torch
+    out = {}
+    for name in ("tiny", "layer2b", "layer1b"):
+        w = synth.WORKLOADS[name]
+        G, m = w["G"], w["m"]
+        f32 = w["dtype"] == "f32"
+        K, V = synth.kv_numpy(w["n_seq"], w["T"], w["outlier_scale"], seed=w["seed"],
+                              dtype=np.float32 if f32 else np.float16)
+        x = torch.from_numpy(np.concatenate([K, V])).to(dev)
+        n_seq, T = x.shape[0], x.shape[1]
+        if name == "tiny":
+            p = nsnq.Params(sub_dim=m, group_size=G)
+            table = torch.empty(nsnq.nsn_table_size(p), dtype=torch.uint8, device=dev)
+            nsnq.nsn_prepare_codebook(p, cb2, table)
+        else:
+            p = nsnq.Params(sub_dim=m, group_size=G)
+            table = table2 if m == 4 else table1
+        codes, meta, shift = (torch.empty(sh, dtype=dt, device=dev) for sh, dt in nsnq.cache_layout(p, n_seq, T))
+        xh = torch.empty_like(x)
+        evq, evd = [], []
+        for i in range(21):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            nsnq.nsn_quantize(p, x, table, codes, meta, shift)
+            b.record(stream)
+            nsnq.nsn_dequantize(p, codes, meta, shift, table, xh)
+            c.record(stream)
+            if i:
+                evq.append((a, b))
+                evd.append((b, c))
+        torch.cuda.synchronize()
+        qms, dms = side_ms(evq), side_ms(evd)
+        ib = 4 if f32 else 2
+        qbytes = quant_bytes(n_seq, T, m, G, ib)
+        dbytes = n_seq * T * (D * ib + D // m + 4) + n_seq * (T // G) * D * 2
+        out[name] = {
+            "shape": f"{n_seq} seqs x {T} tok, {'fp32' if f32 else 'fp16'}, m={m}, G={G}",
+            "quantize_ms": qms, "quantize_gbps": qbytes / (qms * 1e-3) / 1e9,
+            "dequantize_ms": dms, "dequantize_gbps": dbytes / (dms * 1e-3) / 1e9,
+            "quantize_token_heads_per_s": n_seq * T / (qms * 1e-3),
+            "note": "latency-bound at this size, not a roofline measurement",
+        }
+        log(f"{name}: quantize {qms * 1e3:.1f} us, dequantize {dms * 1e3:.1f} us")
+    return out
+
+
+def cpu_baseline(x, cache, G, m, C, C1, qb, ab, R, Nq, scale, step_bytes, n_seq_prefill, synth):
+    """Time the oracle (numpy float64, as it stands) on the host:
+      * the three small workloads whole (quantize + dequantize of every
+        sequence);
+      * the decode workload whole (every (batch, kv head) row: dequantize the
+        cache and attend with its 4 query heads);
+      * the prefill: one of the 16 sequences of a (batch, layer) slice,
+        extrapolated x16 to the slice and x128 to the whole prefill, plus
+        128 of the 2048 sequences of a flush, extrapolated x16.
+    The step's CPU time adds the extrapolated prefill, the decode call, the
+    flush and the dequantize of the flushed group (appends are copies and
+    are not timed).  About 20-30 s of host work."""
     import numpy as np
 
     import oracle
@@ -512,35 +619,64 @@ def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = None
-    # threads the oracle actually runs on: numpy's element-wise work is
-    # single-threaded, its matrix products use the BLAS pool
     affinity = len(os.sched_getaffinity(0))
     cores = blas_threads if blas_threads else 1
-    # quantize sample: whole prefill sequences of 8192 tokens until ~10 s
-    n_tok = 8192
-    tq, n_q = 0.0, 0
-    while tq < 10.0 and n_q < 64:
-        xs = x[n_q, :n_tok].cpu().numpy().astype(np.float64)
+    out = {}
+    # -- the small workloads, whole
+    for name in ("tiny", "layer2b", "layer1b"):
+        w = synth.WORKLOADS[name]
+        f32 = w["dtype"] == "f32"
+        K, V = synth.kv_numpy(w["n_seq"], w["T"], w["outlier_scale"], seed=w["seed"],
+                              dtype=np.float32 if f32 else np.float16)
+        xs = np.concatenate([K, V]).astype(np.float64)
+        Cw = C if w["m"] == 4 else C1
         t0 = time.perf_counter()
-        oracle.quantize(xs, C, G)
-        tq += time.perf_counter() - t0
-        n_q += 1
-    q_rate = quant_bytes(n_q, n_tok, m, G) / tq            # bytes/s
+        for sq in range(xs.shape[0]):
+            co, mo, so = oracle.quantize(xs[sq], Cw, w["G"])
+            oracle.dequantize(co, mo, so, Cw, w["G"])
+        dt = time.perf_counter() - t0
+        nb = quant_bytes(xs.shape[0], w["T"], w["m"], w["G"], 4 if f32 else 2)
+        out[name] = {"seconds": dt, "quantize_dequantize_gbps": nb / dt / 1e9}
+        log(f"cpu oracle {name}: {dt:.2f} s")
+    # -- the decode workload, whole
     kc, vc, kr, vr, q = cache
-    sl = lambda t: t[0:1, 0:1].cpu().numpy()  # noqa: E731
-    k = tuple(sl(t) for t in kc)
-    v = tuple(sl(t) for t in vc)
-    qn = q[0:1, 0:4].cpu().numpy()
-    ta, n_a = 0.0, 0
-    while ta < 5.0 and n_a < 16:
-        t0 = time.perf_counter()
-        oracle.decode_attention(qn, k, v, sl(kr), sl(vr), C, G, Nq, R, scale)
-        ta += time.perf_counter() - t0
-        n_a += 1
-    a_rate = n_a * (Nq * (2 * (128 // m) + 8) + 2 * (Nq // G) * 256 + 2 * R * 256) / ta
-    step_s = qb / q_rate + ab / a_rate
-    log(f"cpu oracle: quantize {q_rate / 1e9:.4f} GB/s ({tq:.1f}s), attention "
-        f"{a_rate / 1e9:.4f} GB/s ({ta:.1f}s)")
+    B3, Hkv = kc[0].shape[0], kc[0].shape[1]
+    Hq = q.shape[1]
+    grp = Hq // Hkv
+    kcn = tuple(t.cpu().numpy() for t in kc)
+    vcn = tuple(t.cpu().numpy() for t in vc)
+    krn, vrn, qn = kr.cpu().numpy(), vr.cpu().numpy(), q.cpu().numpy()
+    t0 = time.perf_counter()
+    for b in range(B3):
+        for h in range(Hkv):
+            sl = lambda t: t[b:b + 1, h:h + 1]  # noqa: E731
+            oracle.decode_attention(qn[b:b + 1, h * grp:(h + 1) * grp], tuple(sl(t) for t in kcn),
+                                    tuple(sl(t) for t in vcn), sl(krn), sl(vrn), C, G, Nq, R, scale)
+    ta = time.perf_counter() - t0
+    out["decode"] = {"seconds": ta, "gbps": ab / ta / 1e9}
+    log(f"cpu oracle decode workload: {ta:.2f} s")
+    # -- prefill: one sequence of a (batch, layer) slice, then x16 x128
+    T = x.shape[1]
+    xs = x[0].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.quantize(xs, C, G)
+    tq1 = time.perf_counter() - t0
+    tq = tq1 * n_seq_prefill
+    out["prefill_sample"] = {"seconds_one_sequence": tq1, "sequence_tokens": T,
+                             "slice_seconds_extrapolated": tq1 * 16,
+                             "prefill_seconds_extrapolated": tq}
+    log(f"cpu oracle prefill: one sequence of {T} tokens in {tq1:.2f} s")
+    # -- flush: 128 of the 2048 sequences, then x16; dequantize of the same
+    nf = 128
+    xf = x[:nf, T - G:].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    res = [oracle.quantize(xf[sq], C, G) for sq in range(nf)]
+    tf = (time.perf_counter() - t0) * (n_seq_prefill / nf)
+    t0 = time.perf_counter()
+    for co, mo, so in res:
+        oracle.dequantize(co, mo, so, C, G)
+    tdq = (time.perf_counter() - t0) * (n_seq_prefill / nf)
+    step_s = tq + ta + tf + tdq
     return {
         "value": step_bytes / step_s / 1e9,
         "unit": "GB/s",
@@ -548,11 +684,13 @@ def cpu_baseline(x, cache, G, m, C, qb, ab, R, Nq, scale, step_bytes):
         "blas_threads": blas_threads,
         "host_cores_available": affinity,
         "kind": "oracle",
-        "sample": (f"oracle.quantize on {n_q} prefill sequences x {n_tok} tokens ({tq:.1f} s) and "
-                   f"oracle.decode_attention {n_a}x on one (batch, kv head) of the decode cache "
-                   f"with its 4 q heads ({ta:.1f} s); step time extrapolated from the two rates"),
-        "quantize_gbps": q_rate / 1e9,
-        "attention_gbps": a_rate / 1e9,
+        "sample": ("small workloads and the decode workload whole; prefill from one of its 2048 "
+                   f"sequences ({tq1:.1f} s, x{n_seq_prefill}); flush and dequantize from {nf} of its "
+                   f"2048 sequences (x{n_seq_prefill // nf}); step time = sum of the parts"),
+        "quantize_gbps": qb / tq / 1e9,
+        "attention_gbps": ab / ta / 1e9,
+        "step_seconds": step_s,
+        "parts": out,
     }
 
 

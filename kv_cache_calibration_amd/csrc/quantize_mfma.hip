@@ -55,6 +55,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kG = 128;
 constexpr int kNW = kG / 32;       // waves per workgroup
 constexpr float kSqrtD = 11.313708498984761f;
+constexpr int kRing = 128;         // queue entries per wave (a ring; 4 KB of the staging tile)
 
 struct alignas(16) QEntry {
   float h[4];
@@ -371,13 +372,36 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) wordv[0][q] = tmain[locate(0, q, offv[0][q])];
 
-  uint32_t codes4[4] = {0u, 0u, 0u, 0u};   // best code of sub-vector k in byte k%4 of word k/4
   // Boxes with five to eight candidates: the first four are evaluated in
   // place; the sub-vector, its other four candidates and its best distance
-  // so far go to a per-wave queue (in the staging tile, free by now), which
-  // the wave then works through one entry per lane, writing an improved code
-  // straight into the owner's result row.
-  QEntry* myq = reinterpret_cast<QEntry*>(&fs.xs[w][0]);
+  // so far go to a per-wave ring (in the staging tile, free by now).
+  // Whenever 64 entries are waiting the wave works through them, one entry
+  // per lane, writing an improved code straight into the owner's result row
+  // (every code is stored as its own byte as soon as it is known, so an
+  // entry may be resolved at any later point).
+  uint8_t* resb = reinterpret_cast<uint8_t*>(&res[w][0][0]);   // lane l: bytes 16 l .. 16 l + 15
+  QEntry* ring = reinterpret_cast<QEntry*>(&fs.xs[w][0]);
+  int qhead = 0, qtail = 0;   // wave-uniform ring positions
+  auto flush = [&](int n) {
+    wave_lds_sync();
+    if (lane < n) {
+      // candidates five to eight are ascending and above the first four, so
+      // a strict '<' against the best so far keeps the lowest code on ties
+      const QEntry e = ring[(qhead + lane) & (kRing - 1)];
+      float bd = e.best;
+      uint32_t bc = 0xffffffffu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
+        const float d = sqdist_cb(e.h, cbh, code, e.ns);
+        bc = d < bd ? code : bc;
+        bd = d < bd ? d : bd;
+      }
+      if (bc != 0xffffffffu) resb[e.dst] = static_cast<uint8_t>(bc);
+    }
+    wave_lds_sync();
+    qhead += n;
+  };
   const uint64_t below = (uint64_t(1) << lane) - 1;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -387,7 +411,6 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       for (int q = 0; q < 4; ++q) wordv[nxt][q] = tmain[locate(mb + 1, q, offv[nxt][q])];
     }
     uint32_t scanmask = 0;   // bit q: sub-vector (mb, q) of this lane needs the full scan
-    int nq = 0;              // queue entries of this step (wave-uniform)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float hv[4] = {acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]};
@@ -396,19 +419,21 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       const bool more4 = cand_more_than_4_lo(lo);
       const bool scan = offv[cur][q] || cand_more_than_8_hi(hi);
       // the four lowest candidates in ascending code order (byte-reversed
-      // when there are more than four), so a strict '<' keeps the lowest code
-      // among equal distances
+      // when there are more than four)
       const uint32_t asc = more4 ? __builtin_amdgcn_perm(0u, lo, 0x00010203u) : lo;
-      float bd = __builtin_huge_valf();
-      uint32_t bc = 0;
+      // distance >= 0 with the candidate's slot in its two low bits: the
+      // integer minimum is the smallest distance (to within 3 ulp) and, among
+      // equal keys, the lowest slot, i.e. the lowest code
+      uint32_t best = 0xffffffffu;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t code = (asc >> (8 * i)) & 0xffu;
         const float d = sqdist_cb(hv, cbh, code, nsc);
-        bc = d < bd ? code : bc;
-        bd = d < bd ? d : bd;
+        best = min(best, (__float_as_uint(d) & ~3u) | static_cast<uint32_t>(i));
       }
-      codes4[mb] |= bc << (8 * q);
+      const uint32_t bc = (asc >> (8 * (best & 3u))) & 0xffu;
+      const uint32_t dst = static_cast<uint32_t>(lane * 16 + 4 * mb + q);
+      resb[dst] = static_cast<uint8_t>(bc);
       scanmask |= scan ? (1u << q) : 0u;
       const bool enq = more4 && !scan;
       const uint64_t bq = __ballot(enq);
@@ -419,12 +444,13 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
         e.h[2] = hv[2];
         e.h[3] = hv[3];
         e.codes = hi;
-        e.best = bd;
-        e.dst = static_cast<uint32_t>(lane * 16 + 4 * mb + q);
+        e.best = __uint_as_float(best & ~3u);
+        e.dst = dst;
         e.ns = nsc;
-        myq[nq + __popcll(bq & below)] = e;
+        ring[(qtail + __popcll(bq & below)) & (kRing - 1)] = e;
       }
-      nq += __popcll(bq);
+      qtail += __popcll(bq);
+      if (qtail - qhead >= kWave) flush(kWave);
     }
     // sub-vectors whose box has more than eight candidates or that lie off
     // the grid: the whole wave scans all codes for one of them at a time
@@ -451,35 +477,15 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
           }
           const float dmin = wave_min_fast(bd);
           const float cmin = wave_min_fast(bd == dmin ? static_cast<float>(bc) : 1e9f);
-          if (lane == src) {
-            const uint32_t c = static_cast<uint32_t>(cmin) & 0xffu;
-            codes4[mb] = (codes4[mb] & ~(0xffu << (8 * q))) | (c << (8 * q));
-          }
+          if (lane == src) resb[lane * 16 + 4 * mb + q] = static_cast<uint8_t>(static_cast<uint32_t>(cmin) & 0xffu);
         }
       }
-    }
-    res[w][lane][mb] = codes4[mb];
-    if (nq > 0) {
-      wave_lds_sync();
-      // candidates five to eight are ascending and above the first four, so
-      // a strict '<' against the best so far keeps the lowest code on ties
-      for (int qi = lane; qi < nq; qi += kWave) {
-        const QEntry e = myq[qi];
-        float bd = e.best;
-        uint32_t bc = 0xffffffffu;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
-          const float d = sqdist_cb(e.h, cbh, code, e.ns);
-          bc = d < bd ? code : bc;
-          bd = d < bd ? d : bd;
-        }
-        if (bc != 0xffffffffu) reinterpret_cast<uint8_t*>(&res[w][0][0])[e.dst] = static_cast<uint8_t>(bc);
-      }
-      wave_lds_sync();
     }
   }
+  if (qtail > qhead) flush(qtail - qhead);
+  uint32_t codes4[4];
   {
+    wave_lds_sync();
     const u32x4 r = *reinterpret_cast<const u32x4*>(&res[w][lane][0]);
     codes4[0] = r.x;
     codes4[1] = r.y;
