@@ -31,6 +31,8 @@ with the authors' system is unpinned (only its stated property is).
 from .nsn import (  # noqa: F401
     hadamard_matrix,
     rotate,
+    rht,
+    rht_inverse,
     normalize_tokens,
     shift_channels,
     nsn,

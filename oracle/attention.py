@@ -25,7 +25,10 @@ residual in the channel domain.  The pin tests check the two agree.
 Pins (tests/test_oracle_attention.py): agreement with a plain per-head loop
 using scipy.special.softmax; the rotated-domain identity; q = 0 gives the
 mean of the values; Nq = 0 gives plain attention over the residual; a single
-key returns its value.
+key returns its value.  With the randomized rotation (``signs``; pins in
+tests/test_oracle_rht.py): the rotated-domain identity again, and equality
+with the plain attention of sign-flipped queries, keys and values, flipped
+back.
 
 ``decode_attention_rope`` is the same attention with the keys stored before
 rotary position embedding, the order the pages give for keys (Methodology
@@ -43,7 +46,7 @@ invariance of the output under a common position shift, and reduction to
 
 import numpy as np
 
-from .nsn import dequantize, rotate
+from .nsn import dequantize, rht, rht_inverse
 
 __all__ = ["attend", "decode_attention", "decode_attention_rotated", "apply_rope",
            "decode_attention_rope"]
@@ -58,20 +61,22 @@ def attend(q, keys, values, scale):
     return p @ np.asarray(values, np.float64)
 
 
-def _kv_rows(cache, b, kvh, n_quant, C, G):
+def _kv_rows(cache, b, kvh, n_quant, C, G, signs=None):
     codes, meta, shift = cache
     if n_quant == 0:
         return np.zeros((0, codes.shape[-1] * C.shape[1]))
     return dequantize(codes[b, kvh, :n_quant], meta[b, kvh, :n_quant],
-                      shift[b, kvh, :n_quant // G], C, G)
+                      shift[b, kvh, :n_quant // G], C, G, signs=signs)
 
 
 def decode_attention(q, k_cache, v_cache, k_resid, v_resid, C, G, n_quant,
-                     n_resid, scale, heads=None):
+                     n_resid, scale, heads=None, signs=None):
     """q: (B, Hq, d); k_cache/v_cache: (codes (B, Hkv, cap, d/m) uint8,
     meta (B, Hkv, cap, 2) fp16, shift (B, Hkv, cap/G, d) fp16);
     k_resid/v_resid: (B, Hkv, Rcap, d) fp16.  Returns float64 (B, Hq, d).
-    ``heads``: optional list of (b, h) pairs to compute (others left NaN)."""
+    ``heads``: optional list of (b, h) pairs to compute (others left NaN).
+    ``signs``: the caches were quantized with the randomized rotation of
+    these channel signs (dequantized with its inverse)."""
     q = np.asarray(q, np.float64)
     B, Hq, d = q.shape
     Hkv = k_cache[0].shape[1]
@@ -82,9 +87,9 @@ def decode_attention(q, k_cache, v_cache, k_resid, v_resid, C, G, n_quant,
     for b, h in todo:
         kvh = h // grp
         if (b, kvh) not in cached:
-            keys = np.concatenate([_kv_rows(k_cache, b, kvh, n_quant, C, G),
+            keys = np.concatenate([_kv_rows(k_cache, b, kvh, n_quant, C, G, signs),
                                    np.asarray(k_resid[b, kvh, :n_resid], np.float64)])
-            vals = np.concatenate([_kv_rows(v_cache, b, kvh, n_quant, C, G),
+            vals = np.concatenate([_kv_rows(v_cache, b, kvh, n_quant, C, G, signs),
                                    np.asarray(v_resid[b, kvh, :n_resid], np.float64)])
             cached = {(b, kvh): (keys, vals)}
         keys, vals = cached[(b, kvh)]
@@ -93,9 +98,11 @@ def decode_attention(q, k_cache, v_cache, k_resid, v_resid, C, G, n_quant,
 
 
 def decode_attention_rotated(q, k_cache, v_cache, k_resid, v_resid, C, G,
-                             n_quant, n_resid, scale):
+                             n_quant, n_resid, scale, signs=None):
     """Same result, with the NSN byproducts folded into the score and the
-    quantized values summed in the rotated domain (one rotation back)."""
+    quantized values summed in the rotated domain (one rotation back).  With
+    ``signs`` the query enters as q' = (H / sqrt(d)) D q and the value sum
+    leaves through D (H / sqrt(d))."""
     q = np.asarray(q, np.float64)
     C = np.asarray(C, np.float64)
     B, Hq, d = q.shape
@@ -105,7 +112,7 @@ def decode_attention_rotated(q, k_cache, v_cache, k_resid, v_resid, C, G,
     for b in range(B):
         for h in range(Hq):
             kvh = h // grp
-            qr = rotate(q[b, h])
+            qr = rht(q[b, h], signs)
             parts_s = []
             if n_quant:
                 kc, km, ks = (a[b, kvh] for a in k_cache)
@@ -129,7 +136,7 @@ def decode_attention_rotated(q, k_cache, v_cache, k_resid, v_resid, C, G,
                 wg = w.reshape(n_quant // G, G).sum(axis=1)
                 acc_rot += wg @ vs[:n_quant // G].astype(np.float64)
             vr = np.asarray(v_resid[b, kvh, :n_resid], np.float64)
-            out[b, h] = rotate(acc_rot) + p[n_quant:] @ vr
+            out[b, h] = rht_inverse(acc_rot, signs) + p[n_quant:] @ vr
     return out
 
 
@@ -168,9 +175,9 @@ def decode_attention_rope(q, k_cache, v_cache, k_resid, v_resid, C, G, n_quant,
     for b, h in todo:
         kvh = h // grp
         if (b, kvh) not in cached:
-            keys = np.concatenate([_kv_rows(k_cache, b, kvh, n_quant, C, G),
+            keys = np.concatenate([_kv_rows(k_cache, b, kvh, n_quant, C, G, signs),
                                    np.asarray(k_resid[b, kvh, :n_resid], np.float64)])
-            vals = np.concatenate([_kv_rows(v_cache, b, kvh, n_quant, C, G),
+            vals = np.concatenate([_kv_rows(v_cache, b, kvh, n_quant, C, G, signs),
                                    np.asarray(v_resid[b, kvh, :n_resid], np.float64)])
             cached = {(b, kvh): (keys, vals)}
         keys, vals = cached[(b, kvh)]

@@ -14,7 +14,13 @@ design notes too):
   * The channel mean of the Shift step runs over groups of ``G`` contiguous
     tokens of one sequence (one (batch, layer, head) of K or of V).
   * The "naive" Hadamard transform is the Sylvester matrix in natural order
-    with orthonormal scaling ``H / sqrt(d)``; no random signs.
+    with orthonormal scaling ``H / sqrt(d)``; no random signs by default.
+  * Randomized variant (``signs``): the rotation becomes ``H D / sqrt(d)``
+    with ``D = diag(signs)``, one +-1 per channel, the flips applied before
+    the transform.  The pages name the randomized transform without fixing
+    how its signs are drawn or shared; reading: one sign vector for the
+    whole cache, drawn by the caller and passed in (so both sides of a test
+    take the same draw).  Dequantization applies the inverse ``D H / sqrt(d)``.
   * Sub-vector ``j`` of a token is the contiguous slice ``h[m*j : m*j+m]``.
   * Nearest codeword = argmin of the exact squared distance; ties go to the
     lowest index.
@@ -33,6 +39,11 @@ NSN with the rotation; moments of NSN+H output approaching N(0,1);
 brute-force nearest codeword by explicit Python loops; product codebooks
 reducing to the scalar Lloyd-Max quantizer; exact ties built from binary
 fractions; the scale-adjust identity; exact round trip with VQ bypassed.
+Randomized variant (tests/test_oracle_rht.py): equality with
+scipy.linalg.hadamard times the sign diagonal, orthonormality, all-plus signs
+reducing to the plain rotation, the exact first two moments of every output
+channel over all 2^d sign vectors at small d, channel-sign equivariance of
+the whole quantizer, and near-unit channel variances on outlier inputs.
 """
 
 import numpy as np
@@ -40,6 +51,8 @@ import numpy as np
 __all__ = [
     "hadamard_matrix",
     "rotate",
+    "rht",
+    "rht_inverse",
     "normalize_tokens",
     "shift_channels",
     "nsn",
@@ -77,6 +90,37 @@ def rotate(u):
     d = u.shape[-1]
     H = hadamard_matrix(d)
     return u @ H.T / np.sqrt(d)
+
+
+def _sign_vector(signs, d):
+    s = np.asarray(signs, dtype=np.float64)
+    if s.shape != (d,) or not np.all(np.abs(s) == 1.0):
+        raise ValueError("signs must be d values of +1 or -1")
+    return s
+
+
+def rht(u, signs=None):
+    """Randomized Hadamard rotation of the last axis: (H / sqrt(d)) D u with
+    D = diag(signs); ``signs=None`` is the plain rotation.
+
+    [NSNQuant summary, Methodology §2: the analysis pairs NSN with the
+    randomized Hadamard transform -- random sign flips of the channels, then
+    the Hadamard matrix -- whose guarantee is that channel variances come out
+    close to 1; the implementation keeps the plain transform.]
+    """
+    u = np.asarray(u, dtype=np.float64)
+    if signs is None:
+        return rotate(u)
+    return rotate(u * _sign_vector(signs, u.shape[-1]))
+
+
+def rht_inverse(h, signs=None):
+    """Inverse of ``rht``: D (H / sqrt(d)) h  (H symmetric with H H = d I,
+    D D = I)."""
+    r = rotate(h)
+    if signs is None:
+        return r
+    return r * _sign_vector(signs, r.shape[-1])
 
 
 def normalize_tokens(x):
@@ -172,11 +216,12 @@ def scale_adjust(h, h_hat):
     return np.where(den > 0, num / safe, 1.0)
 
 
-def quantize(x, C, G, scale_adjust_on=True, return_internals=False):
+def quantize(x, C, G, scale_adjust_on=True, return_internals=False, signs=None):
     """Quantize one sequence x (T, d) against codebook C (K, m).
 
     Steps in the pages' order: Normalize, Shift, Normalize (NSN), Hadamard
-    rotation, nearest codeword per sub-vector, scale adjustment.
+    rotation (randomized by ``signs`` when given), nearest codeword per
+    sub-vector, scale adjustment.
 
     Returns (codes uint8 (T, d/m), meta fp16 (T, 2) = (s1, s2'),
     shift fp16 (T/G, d) = rotated group mean o').  With
@@ -189,13 +234,13 @@ def quantize(x, C, G, scale_adjust_on=True, return_internals=False):
     if K > 256:
         raise ValueError("codes are stored in one byte")
     u, s1, o, s2 = nsn(x, G)
-    h = rotate(u)
+    h = rht(u, signs)
     codes = nearest_codeword(h.reshape(-1, m), C).reshape(T, d // m)
     h_hat = C[codes].reshape(T, d)
     alpha = scale_adjust(h, h_hat) if scale_adjust_on else np.ones(T)
     s2p = s2 * alpha
     meta = np.stack([s1, s2p], axis=-1).astype(np.float16)
-    o_rot = rotate(o)
+    o_rot = rht(o, signs)
     shift = o_rot.astype(np.float16)
     out = (codes.astype(np.uint8), meta, shift)
     if return_internals:
@@ -204,11 +249,12 @@ def quantize(x, C, G, scale_adjust_on=True, return_internals=False):
     return out
 
 
-def dequantize(codes, meta, shift, C, G):
+def dequantize(codes, meta, shift, C, G, signs=None):
     """Reconstruct one sequence from codes and stored fp16 byproducts.
 
     x_hat_t = (H / sqrt(d)) [ s1_t (s2'_t h_hat_t + o'_g) ], the stored fp16
-    numbers taken as exact values.
+    numbers taken as exact values; with ``signs`` the inverse rotation is
+    D (H / sqrt(d)).
     [NSNQuant summary, Methodology §1 (byproducts reconstruct the tensor) and
     §4 (dequantization kernels).]
     """
@@ -223,4 +269,4 @@ def dequantize(codes, meta, shift, C, G):
     s1 = meta[:, 0:1]
     s2p = meta[:, 1:2]
     o_rot = np.repeat(shift, G, axis=0)[:T]
-    return rotate(s1 * (s2p * h_hat + o_rot))
+    return rht_inverse(s1 * (s2p * h_hat + o_rot), signs)

@@ -34,6 +34,7 @@ __all__ = [
     "kv_torch",
     "query_numpy",
     "query_torch",
+    "rht_signs",
 ]
 
 HEAD_DIM = 128
@@ -114,3 +115,11 @@ def query_torch(shape, seed, device, dtype=None):
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return torch.randn(shape, generator=g, device=device, dtype=dtype or torch.float16)
+
+
+def rht_signs(seed, d=HEAD_DIM):
+    """d channel signs (+1.0 / -1.0, float64), each +-1 with probability 1/2,
+    from PCG64(seed): the random diagonal of a randomized Hadamard rotation
+    (drawn here and handed to both sides as an input)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.where(rng.integers(0, 2, size=d) == 1, -1.0, 1.0)
