@@ -161,7 +161,7 @@ def attend_rope(q, keys, values, scale, q_pos, key_pos, base):
 
 
 def decode_attention_rope(q, k_cache, v_cache, k_resid, v_resid, C, G, n_quant,
-                          n_resid, scale, q_pos, base, heads=None):
+                          n_resid, scale, q_pos, base, heads=None, signs=None):
     """``decode_attention`` over keys stored before RoPE: key t of a (b, kv
     head) row (quantized tokens first, then the residual) sits at position t,
     the query at q_pos.  Same arguments plus q_pos and the RoPE base."""
