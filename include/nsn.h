@@ -95,12 +95,29 @@ typedef enum {
  * the fp16 (s1, s2', o') layout. */
 #define NSN_DQ 2u
 
+/* nsn_params.flags: randomized Hadamard rotation (NSNQuant summary,
+ * Methodology §2: the analysis pairs NSN with the randomized transform --
+ * random channel sign flips, then the Hadamard matrix -- which guarantees
+ * channel variances close to 1; the pages' own implementation keeps the
+ * plain transform, which is this library's default).  With this flag the
+ * rotation is R = H D / sqrt(d), D = diag(+-1) given by
+ * nsn_params.rht_signs: bit c % 32 of word c / 32 set means channel c is
+ * negated before H.  The caller draws the signs (any generator) and passes
+ * the same ones to every call on one cache; all zero is the plain rotation.
+ * nsn_quantize stores h and o' in R's frame; nsn_dequantize and
+ * nsn_decode_attention (and _noalloc) invert with D H / sqrt(d).  The
+ * layouts are unchanged and NSN_DQ combines with it.
+ * nsn_decode_attention_rope returns NSN_ERR_UNSUPPORTED with this flag. */
+#define NSN_RHT 4u
+
 typedef struct {
   int32_t head_dim;   /* d: must be 128 */
   int32_t sub_dim;    /* m: 4 (2-bit codes) or 8 (1-bit codes) */
   int32_t n_codes;    /* K: must be 256 (one byte per code) */
   int32_t group_size; /* G: tokens per Shift group; 128 or 256 */
-  uint32_t flags;     /* NSN_SCALE_ADJUST | NSN_DQ, or 0 */
+  uint32_t flags;     /* NSN_SCALE_ADJUST | NSN_DQ | NSN_RHT, or 0 */
+  uint32_t rht_signs[4]; /* NSN_RHT channel signs (see there); ignored
+                            without that flag */
 } nsn_params;
 
 /* Size in bytes of a prepared codebook for these params (codebook, squared

@@ -21,7 +21,7 @@ With double quantization (``Params(dq=True)``, NSN_DQ, G = 128):
 import ctypes
 
 from . import _lib
-from ._lib import NSN_DQ, NSN_SCALE_ADJUST, NsnError  # noqa: F401
+from ._lib import NSN_DQ, NSN_RHT, NSN_SCALE_ADJUST, NsnError  # noqa: F401
 
 __all__ = [
     "Params",
@@ -49,12 +49,26 @@ def lib_path():
 
 
 class Params:
-    """Python view of ``nsn_params``."""
+    """Python view of ``nsn_params``.
+
+    ``rht_signs``: None for the plain Hadamard rotation, or head_dim values
+    of +1 / -1 (channel c negated before the transform where it is -1),
+    packed into the NSN_RHT bit mask."""
 
     def __init__(self, sub_dim=4, group_size=128, scale_adjust=True, head_dim=128, n_codes=256,
-                 dq=False):
-        self.c = _lib.nsn_params(head_dim, sub_dim, n_codes, group_size,
-                                 (NSN_SCALE_ADJUST if scale_adjust else 0) | (NSN_DQ if dq else 0))
+                 dq=False, rht_signs=None):
+        flags = (NSN_SCALE_ADJUST if scale_adjust else 0) | (NSN_DQ if dq else 0)
+        words = [0, 0, 0, 0]
+        if rht_signs is not None:
+            signs = [float(v) for v in rht_signs]
+            if len(signs) != 128 or any(v not in (1.0, -1.0) for v in signs):
+                raise ValueError("rht_signs must be 128 values of +1 or -1")
+            for c, v in enumerate(signs):
+                if v < 0:
+                    words[c // 32] |= 1 << (c % 32)
+            flags |= NSN_RHT
+        self.c = _lib.nsn_params(head_dim, sub_dim, n_codes, group_size, flags,
+                                 (ctypes.c_uint32 * 4)(*words))
 
     @property
     def sub_dim(self):
@@ -67,6 +81,10 @@ class Params:
     @property
     def dq(self):
         return bool(self.c.flags & NSN_DQ)
+
+    @property
+    def rht(self):
+        return bool(self.c.flags & NSN_RHT)
 
 
 def _stride16(t):

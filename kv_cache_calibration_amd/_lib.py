@@ -20,6 +20,7 @@ NSN_F16 = 0
 NSN_F32 = 1
 NSN_SCALE_ADJUST = 1
 NSN_DQ = 2
+NSN_RHT = 4
 
 
 class nsn_params(ctypes.Structure):
@@ -29,6 +30,7 @@ class nsn_params(ctypes.Structure):
         ("n_codes", ctypes.c_int32),
         ("group_size", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("rht_signs", ctypes.c_uint32 * 4),
     ]
 
 

@@ -8,7 +8,9 @@
 //   <q, x_hat_t> = s1_t (s2'_t <q', c(codes_t)> + <q', o'_g>),
 // so keys are never dequantized, and the rotated value sum splits into
 //   sum_t p_t s1_t s2'_t c(codes_t)  +  sum_g o'_g sum_{t in g} p_t s1_t;
-// one inverse rotation per query head at the end gives the output.
+// one inverse rotation per query head at the end gives the output.  The
+// randomized rotation (§2) only changes the two ends: q' = H D q / sqrt(d),
+// and the inverse rotation is followed by D.
 //
 // attn_split_kernel: one workgroup (4 waves) per (token chunk, kv head, block
 //   of up to 4 query heads, batch).  Tile i (64 tokens) of the chunk belongs
@@ -86,6 +88,7 @@ struct SplitParams {
   float scale;
   int64_t q_pos;     // query position (keys stored before rotary embedding)
   float rope_base;   // rotary base, theta_i = base^(-i/64)
+  Signs sg;          // randomized rotation: q' = H D q / sqrt(d) (plain kernel only)
 };
 
 // Double-quantized metadata: per group of the chunk, (lo, step) of the s1
@@ -589,6 +592,11 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
           reinterpret_cast<const uint32_t*>(p.q + (static_cast<int64_t>(b) * p.Hq + h0 + wave) * kD)[lane];
       x0 = h2f(qq & 0xffffu);
       x1 = h2f(qq >> 16);
+    }
+    if (any_sign(p.sg)) {   // randomized rotation: D first
+      const uint32_t wd = sign_word(p.sg, lane >> 4) >> (2 * (lane & 15));
+      x0 = flip_sign(x0, (wd & 1u) << 31);
+      x1 = flip_sign(x1, ((wd >> 1) & 1u) << 31);
     }
     // Walsh-Hadamard transform, channels 2 lane and 2 lane + 1 in this lane
     const float u0 = x0 + x1, u1 = x0 - x1;
@@ -1102,6 +1110,7 @@ struct CombineParams {
   const float* work;
   float* out;
   int Hq, n_split;
+  Signs sg;   // randomized rotation: the inverse ends with D
 };
 
 constexpr int kCombThreads = 256;
@@ -1138,6 +1147,11 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(CombineParam
       const bool up = (lane & e) != 0;
       a0 = up ? y0 - a0 : a0 + y0;
       a1 = up ? y1 - a1 : a1 + y1;
+    }
+    if (any_sign(p.sg)) {
+      const uint32_t wd = sign_word(p.sg, lane >> 4) >> (2 * (lane & 15));
+      a0 = flip_sign(a0, (wd & 1u) << 31);
+      a1 = flip_sign(a1, ((wd >> 1) & 1u) << 31);
     }
   }
   const float* pr = part + p.n_split * kPartStride;
@@ -1229,14 +1243,14 @@ hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t s) {
   SplitParams sp{a.q,     a.kc,       a.vc,    a.km,      a.vm,      a.ks,    a.vs,
                  a.kr,    a.vr,       static_cast<const uint8_t*>(a.table), a.work,
                  a.Hq,    a.Hkv,      grp,     hblocks,   a.n_quant, a.n_split, a.chunk,
-                 a.n_resid, a.cap,    a.rcap,  a.scale,   a.q_pos,   a.rope_base};
+                 a.n_resid, a.cap,    a.rcap,  a.scale,   a.q_pos,   a.rope_base, a.rht};
   hipError_t e;
   if (a.sub_dim == 4)
     e = a.group_size == 128 ? split_launch<4, 128>(a, sp, s) : split_launch<4, 256>(a, sp, s);
   else
     e = a.group_size == 128 ? split_launch<8, 128>(a, sp, s) : split_launch<8, 256>(a, sp, s);
   if (e != hipSuccess) return e;
-  CombineParams cp{a.work, a.out, a.Hq, a.n_split};
+  CombineParams cp{a.work, a.out, a.Hq, a.n_split, a.rht};
   const int per_block = kCombThreads / kWave;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((a.Hq + per_block - 1) / per_block, a.B),
                      dim3(kCombThreads), 0, s, cp);

@@ -57,10 +57,20 @@ nsn_status check_params(const nsn_params* p) {
   if (p->n_codes != 256) return fail(NSN_ERR_UNSUPPORTED, "n_codes must be 256 (got %d)", p->n_codes);
   if (p->group_size != 128 && p->group_size != 256)
     return fail(NSN_ERR_UNSUPPORTED, "group_size must be 128 or 256 (got %d)", p->group_size);
-  if (p->flags & ~(NSN_SCALE_ADJUST | NSN_DQ)) return fail(NSN_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(NSN_SCALE_ADJUST | NSN_DQ | NSN_RHT))
+    return fail(NSN_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   if ((p->flags & NSN_DQ) && p->group_size != 128)
     return fail(NSN_ERR_UNSUPPORTED, "NSN_DQ needs group_size 128 (got %d)", p->group_size);
   return NSN_OK;
+}
+
+// The kernels' sign mask: the caller's with NSN_RHT, else all zero (plain
+// rotation).
+nsn::RhtSigns signs_of(const nsn_params* p) {
+  nsn::RhtSigns r{};
+  if (p->flags & NSN_RHT)
+    for (int i = 0; i < 4; ++i) r.w[i] = p->rht_signs[i];
+  return r;
 }
 
 #define NSN_TRY(expr)            \
@@ -73,7 +83,7 @@ nsn_status check_params(const nsn_params* p) {
 
 extern "C" {
 
-const char* nsn_version(void) { return "nsnq-gfx950 0.1"; }
+const char* nsn_version(void) { return "nsnq-gfx950 0.2"; }
 
 const char* nsn_last_error(void) { return g_err; }
 
@@ -241,6 +251,7 @@ nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype, const void* x, 
                    codes_seq_stride, meta, meta_seq_stride, shift, shift_seq_stride,
                    p->sub_dim, p->group_size, static_cast<int>(p->flags & NSN_SCALE_ADJUST),
                    (p->flags & NSN_DQ) ? 1 : 0};
+  a.rht = signs_of(p);
   return hip_status(nsn::launch_quantize(a, static_cast<hipStream_t>(stream)), "nsn_quantize launch");
 }
 
@@ -279,6 +290,7 @@ nsn_status nsn_dequantize(const nsn_params* p, const uint8_t* codes, int64_t cod
   nsn::DequantArgs a{codes, codes_seq_stride, meta, meta_seq_stride, shift, shift_seq_stride, table,
                      n_seq, n_tok, out_dtype == NSN_F32, x_hat, out_seq_stride, p->sub_dim,
                      p->group_size, (p->flags & NSN_DQ) ? 1 : 0};
+  a.rht = signs_of(p);
   return hip_status(nsn::launch_dequantize(a, static_cast<hipStream_t>(stream)),
                     "nsn_dequantize launch");
 }
@@ -375,6 +387,8 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
                                         float* out, void* stream, const char* what,
                                         bool use_scratch = false) {
   NSN_TRY(check_attn(p, s));
+  if (r && (p->flags & NSN_RHT))
+    return fail(NSN_ERR_UNSUPPORTED, "NSN_RHT is not supported with rotary keys");
   if (!q || !table || (!workspace && !use_scratch) || !out)
     return fail(NSN_ERR_INVALID_ARG, "q, table, workspace and out must be non-NULL");
   if (s->n_quant_tok > 0 && (!k_codes || !k_meta || !k_shift || !v_codes || !v_meta || !v_shift))
@@ -436,6 +450,7 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
   a.rope_base = r ? r->base : 0.f;
   a.q_pos = r ? r->q_pos : 0;
   a.dq = (p->flags & NSN_DQ) ? 1 : 0;
+  a.rht = signs_of(p);
   return hip_status(nsn::launch_decode_attention(a, static_cast<hipStream_t>(stream)), what);
 }
 

@@ -7,6 +7,8 @@
 
 #include <type_traits>
 
+#include "nsn_launch.h"
+
 namespace nsn {
 
 constexpr int kD = 128;      // head_dim
@@ -77,6 +79,26 @@ template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<__half>(__half v) {
   return __half2float(v);
+}
+
+// Channel signs of the randomized Hadamard rotation R = H D / sqrt(d)
+// (RhtSigns): bit c (word c / 32, bit c % 32) set means channel c is negated
+// before H.  All zero for the plain rotation.
+typedef RhtSigns Signs;
+__device__ __forceinline__ bool any_sign(const Signs& s) {
+  return (s.w[0] | s.w[1] | s.w[2] | s.w[3]) != 0u;
+}
+// Word i of the mask for an index that may differ between lanes (a select,
+// never an indexed array: that would go through scratch memory).
+__device__ __forceinline__ uint32_t sign_word(const Signs& s, int i) {
+  return i == 0 ? s.w[0] : (i == 1 ? s.w[1] : (i == 2 ? s.w[2] : s.w[3]));
+}
+// 0x80000000 if channel c is negated, else 0.
+__device__ __forceinline__ uint32_t sign_bit(const Signs& s, int c) {
+  return (sign_word(s, c >> 5) << (31 - (c & 31))) & 0x80000000u;
+}
+__device__ __forceinline__ float flip_sign(float v, uint32_t bit) {
+  return __uint_as_float(__float_as_uint(v) ^ bit);
 }
 
 // In-register unnormalized Walsh-Hadamard transform of N values in Sylvester

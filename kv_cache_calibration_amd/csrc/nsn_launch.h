@@ -12,6 +12,13 @@ namespace nsn {
 // codes, 64 bytes of s1 codes, in uint16 units.
 constexpr int kDqRecU16 = 68;
 
+// Channel signs of the randomized rotation (bit c = channel c negated before
+// the Hadamard transform); all zero for the plain rotation.  Passed to the
+// kernels by value.
+struct RhtSigns {
+  uint32_t w[4];
+};
+
 struct QuantArgs {
   const void* x;
   int in_f32;
@@ -25,6 +32,7 @@ struct QuantArgs {
   int64_t shift_seq_stride;
   int sub_dim, group_size, scale_adjust;
   int dq;   // 1: double-quantized metadata (meta = s2' per token, shift = group records)
+  RhtSigns rht;
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 bool quantize_mfma_supported(int in_f32, int sub_dim, int group_size);
@@ -47,6 +55,7 @@ struct DequantArgs {
   int64_t out_seq_stride;
   int sub_dim, group_size;
   int dq;   // 1: double-quantized metadata
+  RhtSigns rht;
 };
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s);
 
@@ -84,6 +93,7 @@ struct AttnArgs {
   float rope_base;   // rotary base (rope = 1)
   int64_t q_pos;     // query position (rope = 1)
   int dq;            // 1: double-quantized metadata (group_size 128)
+  RhtSigns rht;      // randomized rotation's signs (rope = 0 only)
 };
 // Split choice shared by the workspace-size query and the launch; the
 // rotary kernel (rope = 1) aims at fewer workgroups per CU, so it never needs

@@ -10,7 +10,9 @@
 // This is the same result as the pages' order (NSN, then rotation): the
 // orthonormal rotation keeps token norms (s1, s2 unchanged) and commutes
 // with the group mean (the stored shift is the rotated mean, which is what
-// dequantization and attention consume).
+// dequantization and attention consume).  The randomized rotation (§2)
+// negates the channels its signs select before the transform; the inverse
+// negates them after it.
 #include "nsn_device.h"
 #include "nsn_launch.h"
 
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(G) void quantize_kernel(
     const uint8_t* __restrict__ table, uint8_t* __restrict__ codes,
     int64_t codes_seq_stride, uint16_t* __restrict__ meta,
     int64_t meta_seq_stride, uint16_t* __restrict__ shift,
-    int64_t shift_seq_stride, int scale_adjust) {
+    int64_t shift_seq_stride, int scale_adjust, Signs sg) {
   constexpr int NSUB = kD / M;
   __shared__ float cb[kCodes * M];
   __shared__ float tile[G][33];
@@ -67,6 +69,10 @@ __global__ __launch_bounds__(G) void quantize_kernel(
 
   float v[kD];
   load_row(x + seq * x_seq_stride + tok * kD, v);
+  if (any_sign(sg)) {
+#pragma unroll
+    for (int i = 0; i < kD; ++i) v[i] = flip_sign(v[i], sign_bit(sg, i));
+  }
 
   // Rotation (unnormalized Sylvester transform, then 1/sqrt(d)) and the
   // first token-wise normalization: s1 = ||x|| / sqrt(d).
@@ -185,7 +191,8 @@ template <> __device__ __forceinline__ void store_row<__half>(__half* row, const
 }
 
 // Dequantize [NSNQuant summary §1: the byproducts reconstruct the tensor;
-// §4: dequantization kernel]: x_hat = R [ s1 (s2' c + o') ], R = H/sqrt(d).
+// §4: dequantization kernel]: x_hat = R^T [ s1 (s2' c + o') ], R^T = H/sqrt(d)
+// (D H / sqrt(d) for the randomized rotation).
 // DQ: s1 and o' come from the group's 4-bit record (§3, Double
 // Quantization), s2' from the one-fp16-per-token meta.
 template <typename TOut, int M, int G, bool DQ>
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(G) void dequantize_kernel(
     const uint16_t* __restrict__ meta, int64_t meta_seq_stride,
     const uint16_t* __restrict__ shift, int64_t shift_seq_stride,
     const uint8_t* __restrict__ table, int64_t n_groups, TOut* __restrict__ out,
-    int64_t out_seq_stride) {
+    int64_t out_seq_stride, Signs sg) {
   constexpr int NSUB = kD / M;
   __shared__ float cb[kCodes * M];
   __shared__ float osh[kD];
@@ -243,6 +250,10 @@ __global__ __launch_bounds__(G) void dequantize_kernel(
   fwht_regs<kD>(v);
 #pragma unroll
   for (int i = 0; i < kD; ++i) v[i] *= kInvSqrtD;
+  if (any_sign(sg)) {
+#pragma unroll
+    for (int i = 0; i < kD; ++i) v[i] = flip_sign(v[i], sign_bit(sg, i));
+  }
   store_row<TOut>(out + seq * out_seq_stride + tok * kD, v);
 }
 
@@ -253,7 +264,7 @@ hipError_t quant_launch(const QuantArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((quantize_kernel<TIn, M, G>), dim3(static_cast<unsigned>(blocks)), dim3(G), 0, s,
                      static_cast<const TIn*>(a.x), n_groups, a.x_seq_stride,
                      static_cast<const uint8_t*>(a.table), a.codes, a.codes_seq_stride, a.meta,
-                     a.meta_seq_stride, a.shift, a.shift_seq_stride, a.scale_adjust);
+                     a.meta_seq_stride, a.shift, a.shift_seq_stride, a.scale_adjust, a.rht);
   return hipGetLastError();
 }
 
@@ -264,7 +275,7 @@ hipError_t dequant_launch(const DequantArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((dequantize_kernel<TOut, M, G, DQ>), dim3(static_cast<unsigned>(blocks)), dim3(G), 0, s,
                      a.codes, a.codes_seq_stride, a.meta, a.meta_seq_stride, a.shift,
                      a.shift_seq_stride, static_cast<const uint8_t*>(a.table), n_groups,
-                     static_cast<TOut*>(a.out), a.out_seq_stride);
+                     static_cast<TOut*>(a.out), a.out_seq_stride, a.rht);
   return hipGetLastError();
 }
 

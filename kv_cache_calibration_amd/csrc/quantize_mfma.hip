@@ -16,6 +16,8 @@
 //    j = 8mb + 2q + half, each as four consecutive registers; for m = 8 half
 //    of sub-vector j = 4mb + q.  Channel-major pass (same operand registers,
 //    roles swapped): D[t][c], used for the per-channel group sums.
+//    The randomized rotation (signs given) negates the selected channels of
+//    the staged fp16 input first (sign-bit flips, exact).
 // 2. NSN in the rotated domain: s1 from the token norm, the group mean from
 //    the channel-major pass weighted by 1/s1 (exactly the pages' Shift, since
 //    the rotation is linear and orthonormal), z = y - o', s2 = ||z||/sqrt(d).
@@ -128,7 +130,7 @@ struct FrontSmem {
 // calls it.
 __device__ __forceinline__ void nsn_front(const __half* __restrict__ x, int64_t x_seq_stride,
                                           int64_t seq, int64_t grp, FrontSmem& fs,
-                                          v16f (&acc)[4], float& s1, float& s2) {
+                                          v16f (&acc)[4], float& s1, float& s2, const Signs& sg) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int t = lane & 31, hf = lane >> 5;
@@ -144,6 +146,20 @@ __device__ __forceinline__ void nsn_front(const __half* __restrict__ x, int64_t 
     u32x4 ld[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) ld[i] = load_nt16(wrow + 8 * (kWave * i + lane));
+    if (any_sign(sg)) {
+      // randomized rotation: every load of this lane holds channels 8c ..
+      // 8c + 7 (c = lane % 16) of some token; negate the selected ones by
+      // their fp16 sign bits
+      const int c = lane & 15;
+      const uint32_t byte = (sign_word(sg, c >> 2) >> (8 * (c & 3))) & 0xffu;
+      uint32_t mk[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        mk[k] = (((byte >> (2 * k)) & 1u) << 15) | (((byte >> (2 * k + 1)) & 1u) << 31);
+      const u32x4 m4 = u32x4{mk[0], mk[1], mk[2], mk[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ld[i] ^= m4;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tt = 4 * i + (lane >> 4), c = lane & 15;
@@ -314,7 +330,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
     const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
     const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
     uint16_t* __restrict__ meta, int64_t meta_seq_stride, uint16_t* __restrict__ shift,
-    int64_t shift_seq_stride, int scale_adjust) {
+    int64_t shift_seq_stride, int scale_adjust, Signs sg) {
   // fp16 codebook (the prepared codebook's entries are fp16 values, so this
   // copy is exact and half the LDS traffic of fp32)
   __shared__ __attribute__((aligned(16))) uint32_t cbh[kCodes * 2];
@@ -342,7 +358,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 
   v16f acc[4];
   float s1, s2;
-  nsn_front(x, x_seq_stride, seq, grp, fs, acc, s1, s2);
+  nsn_front(x, x_seq_stride, seq, grp, fs, acc, s1, s2, sg);
 
   // The search runs on z = s2 h directly: distances ||z - s2 c||^2 and bins
   // of z / s2.  A zero z (s2 = 0) is h = 0: scale 1 gives the same answer.
@@ -590,7 +606,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma8_kernel(
     const __half* __restrict__ x, int64_t n_groups, int64_t x_seq_stride,
     const uint8_t* __restrict__ table, uint8_t* __restrict__ codes, int64_t codes_seq_stride,
     uint16_t* __restrict__ meta, int64_t meta_seq_stride, uint16_t* __restrict__ shift,
-    int64_t shift_seq_stride, int scale_adjust) {
+    int64_t shift_seq_stride, int scale_adjust, Signs sg) {
   constexpr int kTiles = kCodes / 32;
   __shared__ __attribute__((aligned(16))) u32x4 cb8[kCodes];        // fp16 codebook [256][8]
   // norm operand of tile T for lane l: fp16 (||c||^2 hi, ||c||^2 lo, 1, 0,
@@ -624,7 +640,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma8_kernel(
 
   v16f acc[4];
   float s1, s2;
-  nsn_front(x, x_seq_stride, seq, grp, fs, acc, s1, s2);   // its barriers publish cb8, a2s
+  nsn_front(x, x_seq_stride, seq, grp, fs, acc, s1, s2, sg);   // its barriers publish cb8, a2s
   // The search runs on g = -2h = z * (-2 / s2) (the factor -2 is exact).  A zero
   // z (s2 = 0) is h = 0: scale 1 gives the same answer.
   const float ginv = -2.0f / (s2 > 0.f ? s2 : 1.0f);
@@ -752,7 +768,7 @@ hipError_t launch_quantize_mfma(const QuantArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kG * 2), 0, s,
                      static_cast<const __half*>(a.x), n_groups, a.x_seq_stride,
                      static_cast<const uint8_t*>(a.table), a.codes, a.codes_seq_stride, a.meta,
-                     a.meta_seq_stride, a.shift, a.shift_seq_stride, a.scale_adjust);
+                     a.meta_seq_stride, a.shift, a.shift_seq_stride, a.scale_adjust, a.rht);
   return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ DQ_TIE = 1e-3
 S1_REL = 4e-6
 
 
-def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128):
+def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128, signs=None):
     """Double-quantized output of one sequence against the oracle run on the
     4-bit codebook C4: codes and s2' as in check_quantized_sequence; in each
     group record lo, hi and the o' scale within one fp16 ulp; where they are
@@ -92,7 +92,7 @@ def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128):
     half a step of the exact ones.  Returns statistics."""
     C64 = np.asarray(C4, np.float64)
     codes_o, meta_o, shift_o, it = oracle.quantize(x, C4, G, scale_adjust_on=scale_adjust,
-                                                   return_internals=True)
+                                                   return_internals=True, signs=signs)
     n_ties = _check_codes(it["h"], C64, codes_g, codes_o)
     _check_s2(it, C64, codes_g, s2_g, scale_adjust)
     _, recs_o = oracle.dq_pack(meta_o, shift_o, it["s1"], it["o_rot"], G)
@@ -134,13 +134,14 @@ def check_dq_sequence(x, C4, codes_g, s2_g, recs_g, scale_adjust=True, G=128):
     return dict(ties=n_ties, codes=codes_o.size, near=n_near, hdr=n_hdr, groups=recs_o.shape[0])
 
 
-def check_quantized_sequence(x, C, G, codes_g, meta_g, shift_g, scale_adjust=True):
-    """Compare one sequence's GPU output to the oracle.  Returns a dict of
-    statistics (number of accepted ties, ...).  Raises AssertionError."""
+def check_quantized_sequence(x, C, G, codes_g, meta_g, shift_g, scale_adjust=True, signs=None):
+    """Compare one sequence's GPU output to the oracle (with the randomized
+    rotation of ``signs`` when given).  Returns a dict of statistics (number
+    of accepted ties, ...).  Raises AssertionError."""
     C64 = np.asarray(C, np.float64)
     m = C64.shape[1]
     codes_o, meta_o, shift_o, it = oracle.quantize(x, C, G, scale_adjust_on=scale_adjust,
-                                                   return_internals=True)
+                                                   return_internals=True, signs=signs)
     n_ties = _check_codes(it["h"], C64, codes_g, codes_o)
     # s1
     s1_o = it["s1"]

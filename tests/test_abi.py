@@ -433,3 +433,31 @@ def test_failed_launch_reports_nsn_err_hip(lib):
     # a later successful call clears the detail string
     assert _q(lib, P(), n_seq=0) == _lib.NSN_OK
     assert lib.nsn_last_error() == b""
+
+
+def test_randomized_rotation_flag(lib):
+    """NSN_RHT is a known flag; the rotary attention call refuses it before
+    touching any pointer; the binding packs +-1 signs into the bit mask
+    (bit c of word c / 32 for a negated channel c)."""
+    import kv_cache_calibration_amd as nsnq
+    RHT = _lib.NSN_SCALE_ADJUST | _lib.NSN_RHT
+    assert lib.nsn_table_size(P(flags=RHT)) > 0
+    assert lib.nsn_table_size(P(flags=RHT | 8)) == 0
+    s = _shape()
+    r = _lib.nsn_rope(10, 10000.0)
+    args = [FAKE] * 10
+    st = lib.nsn_decode_attention_rope(P(flags=RHT), ctypes.byref(s), ctypes.byref(r), *args, FAKE,
+                                       1 << 30, FAKE, NULL)
+    assert st == _lib.NSN_ERR_UNSUPPORTED
+    assert b"NSN_RHT" in lib.nsn_last_error()
+    signs = [1.0] * 128
+    for c in (0, 31, 32, 77, 127):
+        signs[c] = -1.0
+    p = nsnq.Params(rht_signs=signs)
+    assert p.rht and p.c.flags == RHT
+    assert list(p.c.rht_signs) == [(1 << 0) | (1 << 31), 1 << 0, 1 << 13, 1 << 31]
+    assert not nsnq.Params().rht and list(nsnq.Params().c.rht_signs) == [0, 0, 0, 0]
+    with pytest.raises(ValueError):
+        nsnq.Params(rht_signs=[1.0] * 127)
+    with pytest.raises(ValueError):
+        nsnq.Params(rht_signs=[0.0] * 128)
