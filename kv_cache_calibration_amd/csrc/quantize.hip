@@ -1,8 +1,9 @@
 // NSNQuant quantize and dequantize kernels for gfx950.
 //
 // Quantize [NSNQuant summary (gist.science), Methodology §1 NSN, §2 Hadamard,
-// §3 VQ with one global codebook and scale adjustment]: one workgroup per
-// (sequence, token group), one lane per token.  The token's 128 channels
+// §3 VQ with one global codebook and scale adjustment], for the shapes the
+// matrix-core kernels do not take (fp32 input, groups of 256): one workgroup
+// per (sequence, token group), one lane per token.  The token's 128 channels
 // live in VGPRs for the whole pass, so the input is read from HBM exactly
 // once and every intermediate stays on chip.
 //
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(G) void quantize_kernel(
   __shared__ float tile[G][33];
   __shared__ float part[G / 32][32];
   __shared__ float osh[kD];
+  __shared__ __attribute__((aligned(16))) uint8_t binlut[M == 4 ? kFine : 4];   // quantile bin of each fine cell
 
   const int tid = threadIdx.x;
   const int64_t seq = blockIdx.x / n_groups;
@@ -66,6 +68,10 @@ __global__ __launch_bounds__(G) void quantize_kernel(
 
   const float* cbg = reinterpret_cast<const float*>(table + kTabCodebook);
   for (int i = tid; i < kCodes * M; i += G) cb[i] = cbg[i];
+  if constexpr (M == 4) {
+    const uint32_t* bl = reinterpret_cast<const uint32_t*>(table + kTabBinLut);
+    for (int i = tid; i < kFine / 4; i += G) reinterpret_cast<uint32_t*>(binlut)[i] = bl[i];
+  }
 
   float v[kD];
   load_row(x + seq * x_seq_stride + tok * kD, v);
@@ -128,33 +134,75 @@ __global__ __launch_bounds__(G) void quantize_kernel(
     hh = fmaf(v[i], v[i], hh);
   }
 
-  // Nearest codeword of every sub-vector: exact squared distance over all
-  // 256 entries (LDS broadcast reads), strict '<' in index order so ties go
-  // to the lowest index.
+  // Nearest codeword of every sub-vector: the smallest exact squared
+  // distance, ties to the lowest index (the key (distance bits, code) is
+  // minimized; distances are >= 0, so their bits order like their values).
+  // m = 4: the sub-vector's cell of the quantile grid lists every code that
+  // can be nearest anywhere in it (up to eight, one L2-resident u64); cells
+  // with more and points off the grid scan all 256 codes, as m = 8 always
+  // does.
   uint32_t packed[NSUB / 4];
 #pragma unroll
   for (int w = 0; w < NSUB / 4; ++w) packed[w] = 0u;
   float dot = 0.f;
+  const uint64_t* tmain = reinterpret_cast<const uint64_t*>(table + kTabMain);
+  // m = 4: the cells of eight sub-vectors are located first and their eight
+  // table words loaded together, so the lookups' latencies overlap.
+  constexpr int kBatch = M == 4 ? 8 : 1;
 #pragma unroll
-  for (int j = 0; j < NSUB; ++j) {
-    float best = __builtin_huge_valf();
-    int bi = 0;
-#pragma unroll 4
-    for (int k = 0; k < kCodes; ++k) {
-      float d = 0.f;
+  for (int j0 = 0; j0 < NSUB; j0 += kBatch) {
+    uint64_t wv[kBatch];
+    bool off[kBatch];
+    if constexpr (M == 4) {
 #pragma unroll
-      for (int e = 0; e < M; ++e) {
-        const float t = v[M * j + e] - cb[k * M + e];
-        d = fmaf(t, t, d);
-      }
-      if (d < best) {
-        best = d;
-        bi = k;
+      for (int b = 0; b < kBatch; ++b) {
+        int cell = 0;
+        off[b] = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float fe = floorf(fmaf(v[M * (j0 + b) + e], kFineInv, 512.0f));
+          const bool oe = !(fe >= 0.f && fe < static_cast<float>(kFine));   // off the grid or NaN
+          off[b] |= oe;
+          cell = cell * kNB + binlut[oe ? 0 : static_cast<int>(fe)];
+        }
+        wv[b] = tmain[off[b] ? 0 : min(cell, kCells - 1)];
       }
     }
 #pragma unroll
-    for (int e = 0; e < M; ++e) dot = fmaf(v[M * j + e], cb[bi * M + e], dot);
-    packed[j / 4] |= static_cast<uint32_t>(bi) << (8 * (j % 4));
+    for (int b = 0; b < kBatch; ++b) {
+      const int j = j0 + b;
+      uint64_t best = ~uint64_t(0);
+      auto eval = [&](uint32_t k) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < M; ++e) {
+          const float t = v[M * j + e] - cb[k * M + e];
+          d = fmaf(t, t, d);
+        }
+        const uint64_t key = (static_cast<uint64_t>(__float_as_uint(d)) << 32) | k;
+        best = key < best ? key : best;
+      };
+      bool scan = true;
+      if constexpr (M == 4) {
+        scan = off[b] || cand_more_than_8(wv[b]);
+        if (!scan) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) eval(static_cast<uint32_t>(wv[b] >> (8 * i)) & 0xffu);
+          if (cand_more_than_4(wv[b])) {
+#pragma unroll
+            for (int i = 4; i < 8; ++i) eval(static_cast<uint32_t>(wv[b] >> (8 * i)) & 0xffu);
+          }
+        }
+      }
+      if (scan) {
+#pragma unroll 4
+        for (uint32_t k = 0; k < kCodes; ++k) eval(k);
+      }
+      const uint32_t bi = static_cast<uint32_t>(best & 0xffu);
+#pragma unroll
+      for (int e = 0; e < M; ++e) dot = fmaf(v[M * j + e], cb[bi * M + e], dot);
+      packed[j / 4] |= bi << (8 * (j % 4));
+    }
   }
 
   // Scale adjustment: alpha = ||h||^2 / <h, h_hat>, folded into s2.

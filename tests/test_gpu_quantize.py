@@ -66,6 +66,25 @@ def test_quantize_ragged_strided_into_cache(m, G):
                sh[:, off // G:off // G + 3])
 
 
+@pytest.mark.parametrize("G", [128, 256])
+def test_generic_quantizer_off_grid_and_crowded_cells(G):
+    """fp32 input goes through the one-lane-per-token quantizer, whose 2-bit
+    search reads the same candidate tables: tokens equal to rows of the
+    Hadamard matrix rotate to one coordinate of sqrt(128) (off the grid: the
+    full scan), scaled rows plus noise land in sparse outer cells, and the
+    N(0,1) bulk hits cells with more than eight candidates now and then."""
+    _say(f"generic quantizer, fp32, G={G}")
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((2, 2 * G, 128)).astype(np.float32)
+    H = oracle.hadamard_matrix(128)
+    for i, t in enumerate(range(3, 2 * G, 7)):
+        x[i % 2, t] = H[(5 * i) % 128] * (0.5 + i % 3)
+        if i % 2:
+            x[i % 2, t] += 0.3 * rng.standard_normal(128).astype(np.float32)
+    codes, meta, shift, _, (p, table, C) = quantize_gpu(x, 4, G)
+    _check_all(x, C, G, codes, meta, shift)
+
+
 def test_quantize_scale_adjust_off():
     K, _ = synth.kv_numpy(2, 256, 5.0, seed=6, dtype=np.float16)
     codes, meta, shift, _, (p, table, C) = quantize_gpu(K, 4, 128, scale_adjust=False)
