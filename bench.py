@@ -364,6 +364,46 @@ def main():
     ms_attn_dq_rope = side_ms(evadr)
     del cachesq
 
+    # side measurements, outside the step: the randomized Hadamard rotation
+    # (one seeded draw of channel signs), the prefill quantize (its outputs
+    # overwrite the step's) and the decode attention over caches quantized
+    # with the same signs, same shapes
+    pr = nsnq.Params(sub_dim=m, group_size=G, rht_signs=synth.rht_signs(w4["seed"]))
+    evqr = []
+    for i in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nsnq.nsn_quantize(pr, x, table, codes, meta, shift)
+        b.record(stream)
+        if i > 0:
+            evqr.append((a, b))
+    torch.cuda.synchronize()
+    ms_q_rht = side_ms(evqr)
+    cachesr = []
+    for c in range(3):
+        K3, V3 = synth.kv_torch(B3 * Hkv, Nq + R, w3["outlier_scale"], w3["seed"] + 10 * c, dev)
+        kc = torch.empty((B3, Hkv, Nq, D // m), dtype=torch.uint8, device=dev)
+        km = torch.empty((B3, Hkv, Nq, 2), dtype=torch.float16, device=dev)
+        ks = torch.empty((B3, Hkv, Nq // G, D), dtype=torch.float16, device=dev)
+        vc, vm, vs = torch.empty_like(kc), torch.empty_like(km), torch.empty_like(ks)
+        f = lambda t: t.view(B3 * Hkv, *t.shape[2:])  # noqa: E731
+        nsnq.nsn_quantize(pr, K3[:, :Nq], table, f(kc), f(km), f(ks))
+        nsnq.nsn_quantize(pr, V3[:, :Nq], table, f(vc), f(vm), f(vs))
+        cachesr.append(((kc, km, ks), (vc, vm, vs), caches[c][2], caches[c][3], caches[c][4]))
+        del K3, V3
+    evar = []
+    for i in range(max(args.steps, 3) + 1):
+        kcr, vcr, krr, vrr, qr = cachesr[i % 3]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        nsnq.nsn_decode_attention(pr, qr, kcr, vcr, krr, vrr, table, work, out, Nq, R, scale)
+        b.record(stream)
+        if i > 0:
+            evar.append((a, b))
+    torch.cuda.synchronize()
+    ms_attn_rht = side_ms(evar)
+    del cachesr
+
     # side measurement, outside the step: the prefill workload's streaming
     # phase at full size -- 512 decode steps, each appending one token per
     # sequence (2048 sequences, K and V) to the residual window, the window
@@ -426,6 +466,10 @@ def main():
         "attention_dq_ms": ms_attn_dq,
         "attention_dq_rope_gbps": attn_bytes_dq(B3, Hq, Hkv, Nq, R, m, G) / (ms_attn_dq_rope * 1e-3) / 1e9,
         "attention_dq_rope_ms": ms_attn_dq_rope,
+        "quantize_rht_gbps": qb / (ms_q_rht * 1e-3) / 1e9,
+        "quantize_rht_ms": ms_q_rht,
+        "attention_rht_gbps": ab / (ms_attn_rht * 1e-3) / 1e9,
+        "attention_rht_ms": ms_attn_rht,
         "flush_gbps": fb / (ms["flush"] * 1e-3) / 1e9,
         "dequantize_gbps": db / (ms["dequantize"] * 1e-3) / 1e9,
         # sequence positions of the prefill (batch 4 x 131072) per second:
@@ -440,6 +484,8 @@ def main():
     rates["quantize_dq_frac_hbm"] = rates["quantize_dq_gbps"] / HBM_PEAK_GBPS
     rates["attention_dq_frac_hbm"] = rates["attention_dq_gbps"] / HBM_PEAK_GBPS
     rates["attention_dq_rope_frac_hbm"] = rates["attention_dq_rope_gbps"] / HBM_PEAK_GBPS
+    rates["quantize_rht_frac_hbm"] = rates["quantize_rht_gbps"] / HBM_PEAK_GBPS
+    rates["attention_rht_frac_hbm"] = rates["attention_rht_gbps"] / HBM_PEAK_GBPS
     log("kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ms.items()))
     log("rates: " + ", ".join(f"{k} {v:.4g}" for k, v in rates.items()))
 

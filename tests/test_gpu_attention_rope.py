@@ -103,3 +103,28 @@ def test_attention_rope_decode_workload_sampled():
                                             sl(cache["vr"]), cache["C"], w["G"], w["Nq"], w["R"],
                                             1 / math.sqrt(128), q_pos, 10000.0)
         check_attention(got[b, h], want[0, 0], f"rotary (b={b}, h={h})")
+
+
+def test_attention_rope_two_rounds_of_workgroups_sampled():
+    """Twice the decode workload's batch (B = 32): 1024 split workgroups, two
+    rounds at two per CU, so workgroups start on CUs that a finished one left;
+    sampled heads vs the oracle, and two calls give identical bytes."""
+    w = synth.WORKLOADS["decode"]
+    B = 2 * w["B"]
+    print(f"rope attention B={B} (two rounds of workgroups, sampled heads)", flush=True)
+    cache = build_cache(B, w["Hkv"], w["Nq"], w["R"], w["m"], w["G"], seed=w["seed"] + 7,
+                        device_gen=True)
+    q = synth.query_torch((B, w["Hq"], 128), seed=w["seed"] + 8, device=DEV)
+    q_pos = w["Nq"] + w["R"]
+    got = run_rope(cache, q, q_pos, 10000.0)
+    assert np.array_equal(got, run_rope(cache, q, q_pos, 10000.0))
+    qn = q.cpu().numpy()
+    for b, h in ((0, 0), (13, 17), (B - 1, w["Hq"] - 1)):
+        kvh = h // (w["Hq"] // w["Hkv"])
+        sl = lambda t: t[b:b + 1, kvh:kvh + 1].cpu().numpy()  # noqa: E731
+        k = tuple(sl(t) for t in cache["k"])
+        v = tuple(sl(t) for t in cache["v"])
+        want = oracle.decode_attention_rope(qn[b:b + 1, h:h + 1], k, v, sl(cache["kr"]),
+                                            sl(cache["vr"]), cache["C"], w["G"], w["Nq"], w["R"],
+                                            1 / math.sqrt(128), q_pos, 10000.0)
+        check_attention(got[b, h], want[0, 0], f"rotary (b={b}, h={h})")
