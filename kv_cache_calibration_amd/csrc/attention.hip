@@ -29,8 +29,8 @@
 //              p s1 s2' from a per-wave LDS row buffer.
 //     shift    the tile's sum of p s1 per head (fp32) is kept in LDS with the
 //              max it refers to and applied to the group shifts at the end.
-//   The workgroup of chunk 0 first takes the fp16 residual window (exact
-//   scores, original domain), written as partial n_split.
+//   The workgroup of the last chunk first takes the fp16 residual window
+//   (exact scores, original domain), written as partial n_split.
 //   Variants (template flags): ROPE -- keys stored before rotary embedding
 //   (NSNQuant summary §4), scored in the original domain: codewords through
 //   a matrix-core Hadamard, shift, rotation by the key's position, dot
@@ -57,6 +57,7 @@ constexpr int kMaxTiles = kMaxChunk / kTile;
 constexpr int kMaxGroups = kMaxChunk / 128;
 constexpr int kMinChunk = 512;
 constexpr int kMaxResid = 1024;
+constexpr int kResidWeight = 7;      // residual token ~ this many quantized ones (split plan)
 constexpr int kPartStride = 132;     // acc[128], m, l, pad
 constexpr int kBlocksPerCU = 4;      // split workgroups one CU can hold (<= 128 VGPRs)
 constexpr int kPlanBlocksPerCU = 3;  // workgroups per CU the split count aims at (measured best)
@@ -565,9 +566,10 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
     }
     __syncthreads();
   }
-  if (split == 0) {
-    // the residual window first: its load latency overlaps the other
-    // workgroups' work instead of ending the kernel
+  if (split == (p.n_split > 0 ? p.n_split - 1 : 0)) {
+    // the residual window first, in the workgroup of the last chunk (the
+    // plan's shortest): its load latency overlaps the other workgroups' work
+    // instead of ending the kernel
     resid_block<ROPE>(p, smem.r, rsp, theta, b, kvh, hb);
     if (p.n_split == 0) return;
     __syncthreads();   // the LDS is reused
@@ -1192,7 +1194,8 @@ hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s)
 
 }  // namespace
 
-void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int rope, int* n_split, int* chunk) {
+void attn_plan(int B, int Hq, int Hkv, int n_quant, int n_resid, int sub_dim, int group_size, int rope,
+               int* n_split, int* chunk) {
   if (n_quant <= 0) {
     *n_split = 0;
     *chunk = 0;
@@ -1207,7 +1210,14 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int rope, in
   const int64_t max_split = (n_quant + kMinChunk - 1) / kMinChunk;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
-  int64_t c = (n_quant + want - 1) / want;
+  // The last chunk's workgroup also takes the residual window: count each
+  // residual token as kResidWeight quantized ones (its K and V are 512 fp16
+  // bytes against 72 of 2-bit codes and metadata; a 1-bit token takes the
+  // time of a 2-bit one, its codeword gathers being the same size), so that
+  // the chunks come out larger and the last one short by about that much.
+  (void)sub_dim;
+  const int64_t work = n_quant + static_cast<int64_t>(n_resid) * kResidWeight;
+  int64_t c = (work + want - 1) / want;
   c = (c + group_size - 1) / group_size * group_size;
   if (c > kMaxChunk) c = kMaxChunk;
   *chunk = static_cast<int>(c);

@@ -98,7 +98,7 @@ struct AttnArgs {
 // Split choice shared by the workspace-size query and the launch; the
 // rotary kernel (rope = 1) aims at fewer workgroups per CU, so it never needs
 // more workspace than the plain plan the size query reports.
-void attn_plan(int B, int Hq, int Hkv, int n_quant, int group_size, int rope,
+void attn_plan(int B, int Hq, int Hkv, int n_quant, int n_resid, int sub_dim, int group_size, int rope,
                int* n_split, int* chunk);
 // Upper bound of the split count over both plans and every quantized-token
 // count in [0, n_quant]; non-decreasing in n_quant.  The workspace size the
