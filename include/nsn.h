@@ -241,7 +241,9 @@ nsn_status nsn_nearest_codeword(const nsn_params* p, const void* table,
  *          s1 = ||x_t||/sqrt(128) and s2' = s2 * alpha (alpha = 1 without
  *          NSN_SCALE_ADJUST).
  *   shift  fp16 [128] at shift + s*shift_seq_stride + (t/G)*128: the group's
- *          channel mean o, stored rotated (H o / sqrt(128)).
+ *          channel mean o, stored rotated (H o / sqrt(128); with NSN_RHT
+ *          H D o / sqrt(128), and the codes likewise index the sub-vectors
+ *          of the randomized rotation).
  *   With NSN_DQ, meta and shift hold the layouts given at that flag; the
  *   strides are then at least n_tok and (n_tok/128)*68 (multiples of 8 and
  *   4), and in_dtype must be NSN_F16.
@@ -262,8 +264,9 @@ nsn_status nsn_quantize(const nsn_params* p, nsn_dtype in_dtype,
  * nsn_dequantize -- reconstruct tokens from codes and stored byproducts.
  * [NSNQuant summary §1 (the byproducts reconstruct the tensor), §4
  *  (dequantization kernels).]
- * x_hat_t = (H/sqrt(128)) [ s1 (s2' c(codes_t) + o'_g) ], the stored fp16
- * values taken as exact.  Layouts as nsn_quantize; output x_hat
+ * x_hat_t = (H/sqrt(128)) [ s1 (s2' c(codes_t) + o'_g) ] (with NSN_RHT
+ * D H/sqrt(128) [...]), the stored fp16 values taken as exact.  Layouts as
+ * nsn_quantize; output x_hat
  * [n_seq][n_tok][128] of out_dtype, sequences out_seq_stride elements apart.
  * n_tok must be a multiple of group_size; at most 2^24 - 1 token groups per
  * call, as for nsn_quantize.
@@ -312,6 +315,8 @@ typedef struct {
  * and on residual token r: score_r = scale * <q, k_r>.  Softmax over all
  * n_quant_tok + n_resid_tok scores (float32, max-subtracted); values are
  * the dequantized V tokens and the residual V tokens.  No mask, no RoPE.
+ * With NSN_RHT, q' = H D q / sqrt(128) and the values dequantize through
+ * D H / sqrt(128) (the caches must have been quantized with the same signs).
  *
  * q        device fp16 [B][Hq][128].
  * k_codes, v_codes   device uint8 [B][Hkv][cache_capacity][128/m].

@@ -90,21 +90,27 @@ def test_all_plus_signs_give_the_plain_bytes(m):
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("m,G,dt", [(4, 128, torch.float32), (8, 256, torch.float32),
-                                    (4, 128, torch.float16)])
-def test_dequantize_rht_parity(m, G, dt):
+@pytest.mark.parametrize("m,G,dt,dq", [(4, 128, torch.float32, False), (8, 256, torch.float32, False),
+                                       (4, 128, torch.float16, False), (4, 128, torch.float32, True),
+                                       (8, 128, torch.float32, True)])
+def test_dequantize_rht_parity(m, G, dt, dq):
     """GPU dequantization of the GPU's bytes against the oracle's inverse
-    randomized rotation of the same bytes; the plain inverse would be far."""
-    _say(f"dequantize RHT m={m} G={G} {dt}")
+    randomized rotation of the same bytes (double-quantized records decoded
+    first); the plain inverse would be far."""
+    _say(f"dequantize RHT m={m} G={G} {dt} dq={dq}")
     K, V = synth.kv_numpy(2, 1024, 5.0, seed=64, dtype=np.float16)
     x = np.concatenate([K, V])
-    p, table, C = _setup(m, G)
+    p, table, C = _setup(m, G, dq=dq)
     dc, dm, ds = _quantize(p, table, x)
     out = torch.empty((x.shape[0], x.shape[1], 128), dtype=dt, device=DEV)
     nsnq.nsn_dequantize(p, dc, dm, ds, table, out)
     torch.cuda.synchronize()
     xh = out.float().cpu().numpy().astype(np.float64)
     codes, meta, shift = (t.cpu().numpy() for t in (dc, dm, ds))
+    if dq:
+        dec = [oracle.dq_unpack(meta[s], shift[s], G) for s in range(x.shape[0])]
+        meta = np.stack([d[0] for d in dec])
+        shift = np.stack([d[1] for d in dec])
     tol = SAME_BYTES_REL if dt == torch.float32 else 1e-3
     for s in range(x.shape[0]):
         same = oracle.dequantize(codes[s], meta[s], shift[s], C, G, signs=SIGNS)

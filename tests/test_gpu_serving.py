@@ -4,7 +4,9 @@ prefill into a cache with spare capacity, then per step append one token per
 cache at its group offset, and attend (NSNQuant summary, Methodology §4:
 quantized part plus full-precision residual, flushed when full).  The
 attention is compared with the oracle at sampled steps, and the flushed
-cache with one quantize call over the same tokens."""
+cache with one quantize call over the same tokens; plain and
+double-quantized caches, keys before rotary embedding, and the randomized
+rotation."""
 
 import math
 
@@ -34,16 +36,18 @@ def _host(part, B, Hkv, cap, G, dq):
     return c, meta, shift
 
 
-@pytest.mark.parametrize("dq", [False, True])
-@pytest.mark.parametrize("rope", [False, True])
-def test_decode_loop(dq, rope):
+@pytest.mark.parametrize("dq,rope,rht", [(False, False, False), (True, False, False),
+                                         (False, True, False), (True, True, False),
+                                         (False, False, True), (True, False, True)])
+def test_decode_loop(dq, rope, rht):
     m, G, B, Hq, Hkv = 4, 128, 2, 8, 2
     n_seq = B * Hkv
     pre, steps = 3 * G, 2 * G + 37          # an odd number of prefill groups: odd flush offsets
     cap, rcap = ((pre + steps) // G + 2) * G, G
-    print(f"decode loop dq={dq} rope={rope}", flush=True)
+    print(f"decode loop dq={dq} rope={rope} rht={rht}", flush=True)
     C = load_codebook(m)
-    p = nsnq.Params(sub_dim=m, group_size=G, dq=dq)
+    signs = synth.rht_signs(77) if rht else None
+    p = nsnq.Params(sub_dim=m, group_size=G, dq=dq, rht_signs=signs)
     t = torch.empty(nsnq.nsn_table_size(p), dtype=torch.uint8, device=DEV)
     nsnq.nsn_prepare_codebook(p, torch.from_numpy(C).to(DEV), t)
     Cref = oracle.codebook_4bit(C) if dq else C
@@ -89,7 +93,8 @@ def test_decode_loop(dq, rope):
                 want = oracle.decode_attention_rope(q.cpu().numpy(), k, v, krn, vrn, Cref, G, nq, nr,
                                                     scale, nq + nr - 1, 10000.0)
             else:
-                want = oracle.decode_attention(q.cpu().numpy(), k, v, krn, vrn, Cref, G, nq, nr, scale)
+                want = oracle.decode_attention(q.cpu().numpy(), k, v, krn, vrn, Cref, G, nq, nr, scale,
+                                               signs=signs)
             check_attention(out.cpu().numpy(), want, f"decode loop step {step}")
     # the flushed cache equals one quantize call over the same tokens
     kc2 = tuple(torch.zeros(s, dtype=d, device=DEV) for s, d in nsnq.cache_layout(p, n_seq, nq))
