@@ -194,7 +194,43 @@ __global__ __launch_bounds__(G) void quantize_kernel(
           }
         }
       }
-      if (scan) {
+      if constexpr (M == 4) {
+        // The rare sub-vectors that need all 256 codes are scanned by the
+        // whole wave, one at a time: broadcast, four codes per lane, then the
+        // wave minimum of the (distance, code) key.
+        const int lane = tid & (kWave - 1);
+        uint64_t need = __ballot(scan);
+        while (need) {
+          const int l = __builtin_ctzll(need);
+          need &= need - 1;
+          float hb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            hb[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[M * j + e]), l));
+          uint32_t dk = 0xffffffffu, ck = 0xffffffffu;   // this lane's best (distance bits, code)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t k = static_cast<uint32_t>(lane + kWave * r);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float t = hb[e] - cb[k * 4 + e];
+              d = fmaf(t, t, d);
+            }
+            const uint32_t db = __float_as_uint(d);
+            ck = (db < dk || (db == dk && k < ck)) ? k : ck;
+            dk = db < dk ? db : dk;
+          }
+#pragma unroll
+          for (int o = kWave / 2; o >= 1; o >>= 1) {
+            const uint32_t d2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(dk), o, kWave));
+            const uint32_t c2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(ck), o, kWave));
+            ck = (d2 < dk || (d2 == dk && c2 < ck)) ? c2 : ck;
+            dk = d2 < dk ? d2 : dk;
+          }
+          if (lane == l) best = (static_cast<uint64_t>(dk) << 32) | ck;
+        }
+      } else if (scan) {
 #pragma unroll 4
         for (uint32_t k = 0; k < kCodes; ++k) eval(k);
       }
