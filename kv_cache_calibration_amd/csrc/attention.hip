@@ -292,14 +292,12 @@ __device__ __forceinline__ v8h hblk(const HOps& o, int a, int kb) {
   return __builtin_bit_cast(v8h, (kb & 1) ? (neg ? o.N1 : o.P1) : (neg ? o.N0 : o.P0));
 }
 
-// fp16 pair (round to nearest even) of (z0, z1), each rounded once, and the
-// fp16 pair of the remainders (z0 - hi0, z1 - hi1): together about 22
-// significant bits.  Arithmetic only.
+// fp16 pair of (z0, z1), each rounded once toward zero (one instruction for
+// the pair), and the fp16 pair of the remainders (z0 - hi0, z1 - hi1),
+// rounded to nearest even: together about 22 significant bits (the
+// remainder is below one fp16 ulp of z).  Arithmetic only.
 __device__ __forceinline__ uint32_t f16_hi2(float z0, float z1) {
-  uint32_t h;
-  asm("v_fma_mixlo_f16 %0, %1, 1.0, 0 op_sel_hi:[0,0,0]" : "=v"(h) : "v"(z0));
-  asm("v_fma_mixhi_f16 %0, %1, 1.0, 0 op_sel_hi:[0,0,0]" : "+v"(h) : "v"(z1));
-  return h;
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(z0, z1));
 }
 __device__ __forceinline__ uint32_t f16_lo2(float z0, float z1, uint32_t hi) {
   uint32_t l;
