@@ -554,9 +554,11 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
   if constexpr (ROPE) {
     rsp = &rsm;
     theta = rope_theta(p.rope_base, lane);
+    static_assert(kTile == kWave && kThreads % kWave == 0, "one table row per wave pass");
     for (int idx = tid; idx < (kD / 2) * kTile; idx += kThreads) {
+      // i is the same in the whole wave: its frequency is lane i's theta
       const int i = idx / kTile, t = idx % kTile;
-      rsm.tab[i][t] = rope_cs(static_cast<double>(t) * rope_theta(p.rope_base, i));
+      rsm.tab[i][t] = rope_cs(static_cast<double>(t) * __shfl(theta, i, kWave));
     }
     for (int idx = tid; idx < kHB * kD; idx += kThreads) {
       const int h = idx / kD, c = idx % kD;
