@@ -594,13 +594,15 @@ def measured_traffic(src_path, algorithmic_bytes):
 
 def small_workloads(nsnq, synth, table2, table1, cb2, dev, stream):
     """Quantize (+ dequantize) of the tiny, 2-bit layer and 1-bit layer
-    workloads at their stated sizes: median of 20 launches each.  These are
-    too small to fill the chip or to leave the caches (the tiny one is two
-    workgroups) and take microseconds, so launch latency dominates: reported
-    for completeness, not as roofline measurements."""
+    workloads at their stated sizes: median of 20 launches each, with the
+    Infinity Cache and L2 evicted before each (512 MiB written).  These are
+    too small to fill the chip (the tiny one is two workgroups) and take
+    microseconds, so launch latency dominates: reported for completeness,
+    not as roofline measurements."""
     import numpy as np
     import torch
     out = {}
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for name in ("tiny", "layer2b", "layer1b"):
         w = synth.WORKLOADS[name]
         G, m = w["G"], w["m"]
@@ -621,6 +623,7 @@ def small_workloads(nsnq, synth, table2, table1, cb2, dev, stream):
         evq, evd = [], []
         for i in range(21):
             a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            evict.fill_(i & 255)
             a.record(stream)
             nsnq.nsn_quantize(p, x, table, codes, meta, shift)
             b.record(stream)
@@ -639,9 +642,10 @@ def small_workloads(nsnq, synth, table2, table1, cb2, dev, stream):
             "quantize_ms": qms, "quantize_gbps": qbytes / (qms * 1e-3) / 1e9,
             "dequantize_ms": dms, "dequantize_gbps": dbytes / (dms * 1e-3) / 1e9,
             "quantize_token_heads_per_s": n_seq * T / (qms * 1e-3),
-            "note": "latency-bound at this size, not a roofline measurement",
+            "note": "latency-bound at this size, not a roofline measurement (cold Infinity Cache)",
         }
         log(f"{name}: quantize {qms * 1e3:.1f} us, dequantize {dms * 1e3:.1f} us")
+    del evict
     return out
 
 

@@ -4,7 +4,8 @@
  * The method: each KV token of one head (d = 128 channels) is normalized to
  * norm sqrt(d) (scale s1), centred by the per-channel mean of its token
  * group (o), normalized again (s2), rotated by the orthonormal Hadamard
- * transform, and every m-dimensional sub-vector (m = 4: 2 bits per value,
+ * transform (optionally randomized by channel signs, NSN_RHT), and every
+ * m-dimensional sub-vector (m = 4: 2 bits per value,
  * m = 8: 1 bit) is replaced by the index of its nearest codeword in one
  * 256-entry codebook built by k-means on standard-normal samples.
  * [NSNQuant technical summary (gist.science, es/de), Methodology §1 NSN,
