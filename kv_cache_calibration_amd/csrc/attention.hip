@@ -1194,7 +1194,7 @@ hipError_t split_launch(const AttnArgs& a, const SplitParams& sp, hipStream_t s)
 
 }  // namespace
 
-void attn_plan(int B, int Hq, int Hkv, int n_quant, int n_resid, int sub_dim, int group_size, int rope,
+void attn_plan(int B, int Hq, int Hkv, int n_quant, int n_resid, int group_size, int rope,
                int* n_split, int* chunk) {
   if (n_quant <= 0) {
     *n_split = 0;
@@ -1215,7 +1215,6 @@ void attn_plan(int B, int Hq, int Hkv, int n_quant, int n_resid, int sub_dim, in
   // bytes against 72 of 2-bit codes and metadata; a 1-bit token takes the
   // time of a 2-bit one, its codeword gathers being the same size), so that
   // the chunks come out larger and the last one short by about that much.
-  (void)sub_dim;
   const int64_t work = n_quant + static_cast<int64_t>(n_resid) * kResidWeight;
   int64_t c = (work + want - 1) / want;
   c = (c + group_size - 1) / group_size * group_size;

@@ -402,9 +402,8 @@ static nsn_status decode_attention_impl(const nsn_params* p, const nsn_attn_shap
   if ((k_shift && !shift_aligned(p, k_shift)) || (v_shift && !shift_aligned(p, v_shift)))
     return fail(NSN_ERR_INVALID_ARG, "shift pointers must be 16-byte aligned (8 with NSN_DQ)");
   int n_split = 0, chunk = 0;
-  nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, s->n_resid_tok, p->sub_dim,
-                 p->group_size, r ? 1 : 0,
-                 &n_split, &chunk);
+  nsn::attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->n_quant_tok, s->n_resid_tok, p->group_size,
+                 r ? 1 : 0, &n_split, &chunk);
   // the size query's monotone bound, so one workspace sized for a cache
   // serves every fill level of it
   const size_t need = nsn::attn_workspace_bytes(

@@ -95,10 +95,11 @@ struct AttnArgs {
   int dq;            // 1: double-quantized metadata (group_size 128)
   RhtSigns rht;      // randomized rotation's signs (rope = 0 only)
 };
-// Split choice shared by the workspace-size query and the launch; the
-// rotary kernel (rope = 1) aims at fewer workgroups per CU, so it never needs
-// more workspace than the plain plan the size query reports.
-void attn_plan(int B, int Hq, int Hkv, int n_quant, int n_resid, int sub_dim, int group_size, int rope,
+// Split choice of one launch: chunks of whole groups, the last one shortened
+// for the residual window its workgroup also takes (n_resid); the rotary
+// kernel (rope = 1) aims at fewer workgroups per CU.  Never above
+// attn_split_bound, which sizes the workspace.
+void attn_plan(int B, int Hq, int Hkv, int n_quant, int n_resid, int group_size, int rope,
                int* n_split, int* chunk);
 // Upper bound of the split count over both plans and every quantized-token
 // count in [0, n_quant]; non-decreasing in n_quant.  The workspace size the

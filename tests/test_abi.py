@@ -201,11 +201,19 @@ def test_attention_workspace_covers_every_fill_level(lib):
         assert all(a <= b for a, b in zip(sizes, sizes[1:])), (B, Hq, Hkv, G)
         full = sizes[-1]
         args = [FAKE] * 10
+        r = _lib.nsn_rope(10, 10000.0)
         for n in range(G, cap + 1, G):
-            s = _lib.nsn_attn_shape(B, Hq, Hkv, n, 1, cap, 1, 0.088)
-            # one byte short of the query's answer at n: rejected before any launch
-            st = lib.nsn_decode_attention(P(G=G), ctypes.byref(s), *args, FAKE, size(n) - 1, FAKE, NULL)
-            assert st == _lib.NSN_ERR_WORKSPACE
+            # the plan depends on the residual length too (the last chunk is
+            # shortened for it); the size query does not, and must cover it
+            for nr in (0, 1, 77, 1024):
+                s = _lib.nsn_attn_shape(B, Hq, Hkv, n, nr, cap, max(nr, 1), 0.088)
+                # one byte short of the query's answer at n: rejected before any
+                # launch (a plan above the bound would say NSN_ERR_INTERNAL)
+                st = lib.nsn_decode_attention(P(G=G), ctypes.byref(s), *args, FAKE, size(n) - 1, FAKE, NULL)
+                assert st == _lib.NSN_ERR_WORKSPACE, (B, Hq, Hkv, G, n, nr, st)
+                st = lib.nsn_decode_attention_rope(P(G=G), ctypes.byref(s), ctypes.byref(r), *args, FAKE,
+                                                   size(n) - 1, FAKE, NULL)
+                assert st == _lib.NSN_ERR_WORKSPACE, (B, Hq, Hkv, G, n, nr, st)
             assert size(n) <= full
 
 
