@@ -146,6 +146,9 @@ __global__ __launch_bounds__(256) void tab_write_kernel(uint8_t* __restrict__ ta
 
 // Stand-alone nearest codeword of arbitrary sub-vectors (one thread each),
 // using the same tables and the same lexicographic (distance, code) key.
+// m = 4: a sub-vector in a crowded or off-grid cell is scanned over all 256
+// codes by the whole wave (four codes per lane, then the wave minimum), as
+// the quantizers do; m = 8 scans per lane.
 template <int M>
 __global__ __launch_bounds__(256) void nearest_kernel(const uint8_t* __restrict__ table,
                                                       const float* __restrict__ v, int64_t n,
@@ -155,22 +158,24 @@ __global__ __launch_bounds__(256) void nearest_kernel(const uint8_t* __restrict_
   for (int i = threadIdx.x; i < kCodes * M; i += 256) cb[i] = cbg[i];
   __syncthreads();
   const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (id >= n) return;
+  const bool valid = id < n;   // lanes past the end still join the wave scans
   float h[M];
 #pragma unroll
-  for (int e = 0; e < M; ++e) h[e] = v[id * M + e];
+  for (int e = 0; e < M; ++e) h[e] = valid ? v[id * M + e] : 0.f;
   uint64_t best = ~uint64_t(0);
-  auto eval = [&](uint32_t k) {
+  auto dist = [&](const float (&x)[M], uint32_t k) {
     float d = 0.f;
 #pragma unroll
     for (int e = 0; e < M; ++e) {
-      const float t = h[e] - cb[k * M + e];
+      const float t = x[e] - cb[k * M + e];
       d = (e == 0) ? t * t : fmaf(t, t, d);
     }
-    const uint64_t key = (static_cast<uint64_t>(__float_as_uint(d)) << 32) | k;
+    return d;
+  };
+  auto eval = [&](uint32_t k) {
+    const uint64_t key = (static_cast<uint64_t>(__float_as_uint(dist(h, k))) << 32) | k;
     best = key < best ? key : best;
   };
-  bool brute = true;
   if constexpr (M == 4) {
     int cell = 0;
     bool off = false;
@@ -180,6 +185,7 @@ __global__ __launch_bounds__(256) void nearest_kernel(const uint8_t* __restrict_
       cell = cell * kNB + (off ? 0 : table[kTabBinLut + static_cast<int>(fe)]);
     }
     cell = min(cell, kCells - 1);   // in bounds even for an unprepared table
+    bool brute = true;
     if (!off) {
       const uint64_t wv = reinterpret_cast<const uint64_t*>(table + kTabMain)[cell];
       brute = cand_more_than_8(wv);
@@ -189,10 +195,35 @@ __global__ __launch_bounds__(256) void nearest_kernel(const uint8_t* __restrict_
           for (int i = 4; i < 8; ++i) eval(static_cast<uint32_t>(wv >> (8 * i)) & 0xffu);
       }
     }
-  }
-  if (brute)
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t need = __ballot(valid && brute);
+    while (need) {
+      const int l = __builtin_ctzll(need);
+      need &= need - 1;
+      float hb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hb[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h[e]), l));
+      uint32_t dk = 0xffffffffu, ck = 0xffffffffu;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t k = static_cast<uint32_t>(lane + kWave * r);
+        const uint32_t db = __float_as_uint(dist(hb, k));
+        ck = (db < dk || (db == dk && k < ck)) ? k : ck;
+        dk = db < dk ? db : dk;
+      }
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) {
+        const uint32_t d2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(dk), o, kWave));
+        const uint32_t c2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(ck), o, kWave));
+        ck = (d2 < dk || (d2 == dk && c2 < ck)) ? c2 : ck;
+        dk = d2 < dk ? d2 : dk;
+      }
+      if (lane == l) best = (static_cast<uint64_t>(dk) << 32) | ck;
+    }
+  } else {
     for (uint32_t k = 0; k < kCodes; ++k) eval(k);
-  out[id] = static_cast<uint8_t>(best & 0xffu);
+  }
+  if (valid) out[id] = static_cast<uint8_t>(best & 0xffu);
 }
 
 }  // namespace
