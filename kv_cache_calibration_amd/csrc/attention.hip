@@ -957,7 +957,12 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
 #pragma unroll
     for (int h = 0; h < kHB; ++h) s[h] = ks * fmaf(s2k, dot[h], qov[h]);
     }
-    // -- running max, raised only when a score exceeds it
+    // -- running max, raised only when a score exceeds it.  From here to the
+    //    end of the value phase the wave runs at raised issue priority, so a
+    //    wave that holds its scores finishes the tile while the others gather
+    //    codewords for theirs (measured 2-3.5 % faster than one priority;
+    //    the rotary kernel, whose score phase dominates, keeps one).
+    if constexpr (!ROPE) __builtin_amdgcn_s_setprio(1);
     bool raised = false;
     float fl = 1.f;
 #pragma unroll
@@ -1026,6 +1031,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       const u32x4 bw = u32x4{w0.x, w0.y, w1.x, w1.y};
       value_steps<M, 0>(acc, d, kb, bw, cbh_base);
     }
+    if constexpr (!ROPE) __builtin_amdgcn_s_setprio(0);
     if (more) load_values<M>(d, vcrow + tn * kTile * CB, voff);
     wave_lds_sync();
   }
