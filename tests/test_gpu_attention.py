@@ -202,3 +202,105 @@ def test_attention_long_context_many_chunks():
     assert ws == B * Hq * (256 + 1) * 132 * 4
     q = synth.query_torch((B, Hq, 128), seed=96, device=DEV)
     check(cache, q)
+
+
+def test_attention_any_workspace_contents_and_graph_replay():
+    """The output does not depend on what the workspace held (every partial is
+    written before it is read): all-ones, zero and random bytes, a workspace
+    just used by a call with another split count, and replays of a captured
+    HIP graph (eager calls and synchronizations in between) all give the same
+    bytes, which match the oracle."""
+    B, Hq, Hkv, Nq, R, m, G = 2, 8, 2, 4096, 16, 4, 128
+    print("attention: workspace contents and graph replay", flush=True)
+    cache = build_cache(B, Hkv, Nq, R, m, G, seed=97)
+    q = synth.query_torch((B, Hq, 128), seed=98, device=DEV)
+    scale = 1 / math.sqrt(128)
+    p = cache["p"]
+    ws = nsnq.nsn_decode_attention_workspace_size(p, B, Hq, Hkv, Nq, R, Nq, R, scale)
+    work = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+
+    def launch(nq):
+        nsnq.nsn_decode_attention(p, q, cache["k"], cache["v"], cache["kr"], cache["vr"],
+                                  cache["table"], work, out, nq, R, scale)
+
+    def call(nq=Nq):
+        out.fill_(float("nan"))
+        launch(nq)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    work.fill_(255)
+    ref = call()
+    k, v, kr, vr = to_np(cache)
+    want = oracle.decode_attention(q.cpu().numpy(), k, v, kr, vr, cache["C"], G, Nq, R, scale)
+    check_attention(ref, want)
+    work.zero_()
+    assert np.array_equal(call(), ref)
+    work.copy_(torch.randint(0, 256, (ws,), dtype=torch.uint8, device=DEV))
+    assert np.array_equal(call(), ref)
+    # fewer chunks (a shorter fill of the same cache) on the same workspace
+    short = call(1024)
+    assert np.isfinite(short).all() and not np.array_equal(short, ref)
+    assert np.array_equal(call(), ref)
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch(Nq)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        launch(Nq)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert np.array_equal(call(1024), short)      # eager work between replays
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref), f"replay {i}"
+
+
+def test_attention_repeated_calls_many_workgroups():
+    """768 split workgroups (six chunks per head block, spread over every XCD)
+    and the merge launch: 24 calls queued on one workspace alternate between
+    two query sets, and every output is bit-identical to the first output of
+    its query set -- a partial of the other set's call read by a merge would
+    show.  The first outputs match the oracle on sampled heads."""
+    B, Hq, Hkv, Nq, R, m, G = 16, 32, 8, 8192, 128, 4, 128
+    print("attention: repeated calls, 768 workgroups", flush=True)
+    cache = build_cache(B, Hkv, Nq, R, m, G, seed=101, device_gen=True)
+    scale = 1 / math.sqrt(128)
+    p = cache["p"]
+    ws = nsnq.nsn_decode_attention_workspace_size(p, B, Hq, Hkv, Nq, R, Nq, R, scale)
+    work = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    qs = [synth.query_torch((B, Hq, 128), seed=102 + i, device=DEV) for i in range(2)]
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV) for _ in range(2)]
+
+    def launch(i):
+        outs[i].fill_(float("nan"))
+        nsnq.nsn_decode_attention(p, qs[i], cache["k"], cache["v"], cache["kr"], cache["vr"],
+                                  cache["table"], work, outs[i], Nq, R, scale)
+
+    refs = []
+    for i in range(2):
+        launch(i)
+        torch.cuda.synchronize()
+        refs.append(outs[i].cpu().numpy())
+    assert not np.array_equal(refs[0], refs[1])
+    for b, h in [(0, 0), (9, 17), (B - 1, Hq - 1)]:
+        kvh = h // (Hq // Hkv)
+        sl = lambda t: t[b:b + 1, kvh:kvh + 1].cpu().numpy()  # noqa: E731
+        k = tuple(sl(t) for t in cache["k"])
+        v = tuple(sl(t) for t in cache["v"])
+        for i in range(2):
+            want = oracle.decode_attention(qs[i].cpu().numpy()[b:b + 1, h:h + 1], k, v, sl(cache["kr"]),
+                                           sl(cache["vr"]), cache["C"], G, Nq, R, scale)
+            check_attention(refs[i][b, h], want[0, 0], f"(b={b}, h={h}, q set {i})")
+    for r in range(12):
+        launch(0)
+        launch(1)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert np.array_equal(outs[i].cpu().numpy(), refs[i]), f"round {r}, query set {i}"
