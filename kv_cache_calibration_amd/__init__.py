@@ -130,10 +130,25 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+_raw_stream = None
+
+
 def _stream(stream):
+    """HIP stream handle of the call: the given torch stream, else torch's
+    current stream on the current device.  The latter is read through
+    torch's raw getter when it exists (building a Stream object costs more
+    than the kernel launch of a small call)."""
+    global _raw_stream
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_stream is None:
+        getter = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if getter is not None:
+            _raw_stream = lambda: getter(torch.cuda.current_device())  # noqa: E731
+        else:
+            _raw_stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    return ctypes.c_void_p(_raw_stream())
 
 
 def _dev(*ts):
