@@ -39,6 +39,7 @@ __all__ = [
     "nsn_decode_attention_rope",
     "nsn_decode_attention_noalloc",
     "nsn_decode_attention_workspace_size",
+    "PreparedDecodeAttention",
     "lib_path",
     "cache_layout",
 ]
@@ -400,18 +401,24 @@ def _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out):
             raise ValueError("residuals must be (B, Hkv, Rcap, 128), alike for K and V")
 
 
-def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
-                      n_quant_tok, n_resid_tok, softmax_scale, stream, rope, noalloc=False):
+def _check_attention_call(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out):
     kc, km, ks = k_cache
     vc, vm, vs = v_cache
     _dev(q, kc, km, ks, vc, vm, vs, k_resid, v_resid, table, workspace, out)
     for t in (q, kc, km, ks, vc, vm, vs, k_resid, v_resid, out):
         if not t.is_contiguous():
             raise ValueError("attention tensors must be contiguous")
-    B, Hq, _ = q.shape
-    Hkv, cap = kc.shape[1], kc.shape[2]
     _check_attention_shapes(params, q, k_cache, v_cache, k_resid, v_resid, out)
     _check_table(params, table)
+
+
+def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
+                      n_quant_tok, n_resid_tok, softmax_scale, stream, rope, noalloc=False):
+    kc, km, ks = k_cache
+    vc, vm, vs = v_cache
+    _check_attention_call(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out)
+    B, Hq, _ = q.shape
+    Hkv, cap = kc.shape[1], kc.shape[2]
     s = _shape(B, Hq, Hkv, n_quant_tok, n_resid_tok, cap, k_resid.shape[2], softmax_scale)
     lib = _lib.load()
     if noalloc:
@@ -427,3 +434,48 @@ def _decode_attention(params, q, k_cache, v_cache, k_resid, v_resid, table, work
     else:
         _lib.check(lib.nsn_decode_attention_rope(ctypes.byref(params.c), ctypes.byref(s),
                                                  ctypes.byref(rope), *bufs))
+
+
+class PreparedDecodeAttention:
+    """nsn_decode_attention -- or nsn_decode_attention_rope when ``rope_base``
+    is given -- with its tensors checked and marshalled once, for a decode
+    loop that passes the same buffers every step.
+
+    Calling the object with the step's token counts (and the query position
+    for rotary keys) sets them in the shape struct and makes the library
+    call, which still validates every argument; the tensors' devices,
+    dtypes, shapes and contiguity are checked here once, so they must keep
+    their shapes afterwards (the object holds references to them, so they
+    stay allocated).  Results equal those of the per-call function."""
+
+    def __init__(self, params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out,
+                 softmax_scale, rope_base=None):
+        _check_attention_call(params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out)
+        kc, km, ks = k_cache
+        vc, vm, vs = v_cache
+        self._keep = (params, q, k_cache, v_cache, k_resid, v_resid, table, workspace, out)
+        self._s = _shape(q.shape[0], q.shape[1], kc.shape[1], 0, 0, kc.shape[2], k_resid.shape[2],
+                         softmax_scale)
+        self._args = [ctypes.byref(params.c), ctypes.byref(self._s)]
+        self._rope = None
+        lib = _lib.load()
+        if rope_base is not None:
+            self._rope = _lib.nsn_rope(0, float(rope_base))
+            self._args.append(ctypes.byref(self._rope))
+            self._fn = lib.nsn_decode_attention_rope
+        else:
+            self._fn = lib.nsn_decode_attention
+        self._args += [_ptr(q), _ptr(kc), _ptr(km), _ptr(ks), _ptr(vc), _ptr(vm), _ptr(vs),
+                       _ptr(k_resid), _ptr(v_resid), _ptr(table), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _ptr(out)]
+
+    def __call__(self, n_quant_tok, n_resid_tok, q_pos=None, stream=None):
+        self._s.n_quant_tok = n_quant_tok
+        self._s.n_resid_tok = n_resid_tok
+        if self._rope is not None:
+            if q_pos is None:
+                raise ValueError("q_pos is required with rotary keys")
+            self._rope.q_pos = q_pos
+        status = self._fn(*self._args, _stream(stream))
+        if status != _lib.NSN_OK:
+            _lib.check(status)

@@ -374,6 +374,28 @@ def test_binding_rejects_wrong_dtypes_and_sizes():
         nsnq._check_attention_shapes(p, q, plain, plain, kr.float(), kr, out)
 
 
+def test_prepared_attention_checks_its_tensors_once():
+    """PreparedDecodeAttention runs the per-call function's checks at
+    construction: host tensors, a wrong dtype or a short table are refused
+    before anything is marshalled (no GPU needed)."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    p = nsnq.Params(sub_dim=4)
+    B, Hq, Hkv, cap, R = 1, 4, 1, 128, 4
+    kc = torch.zeros((B, Hkv, cap, 32), dtype=torch.uint8)
+    plain = (kc, torch.zeros((B, Hkv, cap, 2), dtype=torch.float16),
+             torch.zeros((B, Hkv, 1, 128), dtype=torch.float16))
+    kr = torch.zeros((B, Hkv, R, 128), dtype=torch.float16)
+    q = torch.zeros((B, Hq, 128), dtype=torch.float16)
+    out = torch.zeros((B, Hq, 128), dtype=torch.float32)
+    table = torch.zeros(16, dtype=torch.uint8)
+    work = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):
+        nsnq.PreparedDecodeAttention(p, q, plain, plain, kr, kr, table, work, out, 0.1)
+    with pytest.raises(ValueError):
+        nsnq._check_attention_call(p, q.float(), plain, plain, kr, kr, table, work, out)
+
+
 def test_binding_checks_sequence_and_group_extents():
     """The C ABI trusts the sequence count and the group slots it is given:
     the binding rejects codes, meta or shift tensors with fewer sequences

@@ -304,3 +304,44 @@ def test_attention_repeated_calls_many_workgroups():
         torch.cuda.synchronize()
         for i in range(2):
             assert np.array_equal(outs[i].cpu().numpy(), refs[i]), f"round {r}, query set {i}"
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_prepared_call_matches_per_call(rope):
+    """A decode loop through PreparedDecodeAttention (tensors checked once,
+    token counts and query position set per step) gives the bytes of the
+    per-call function at every step; a missing q_pos with rotary keys and a
+    count above the cache are refused."""
+    B, Hq, Hkv, Nq, R, m, G = 2, 8, 2, 2048, 40, 4, 128
+    print(f"prepared attention call, rope={rope}", flush=True)
+    cache = build_cache(B, Hkv, Nq, R, m, G, seed=111, rcap=64)
+    p = cache["p"]
+    q = synth.query_torch((B, Hq, 128), seed=112, device=DEV)
+    scale = 1 / math.sqrt(128)
+    ws = nsnq.nsn_decode_attention_workspace_size(p, B, Hq, Hkv, Nq, 64, Nq, 64, scale)
+    work = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    out_a = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    out_b = torch.empty_like(out_a)
+    base = 10000.0
+    call = nsnq.PreparedDecodeAttention(p, q, cache["k"], cache["v"], cache["kr"], cache["vr"],
+                                        cache["table"], work, out_a, scale,
+                                        rope_base=base if rope else None)
+    for nq, r in [(0, 5), (128, 0), (640, 17), (1024, 40), (2048, 1), (2048, 40)]:
+        q_pos = nq + r + 3
+        out_a.fill_(float("nan"))
+        out_b.fill_(float("nan"))
+        call(nq, r, q_pos=q_pos if rope else None)
+        if rope:
+            nsnq.nsn_decode_attention_rope(p, q, cache["k"], cache["v"], cache["kr"], cache["vr"],
+                                           cache["table"], work, out_b, nq, r, scale, q_pos, base)
+        else:
+            nsnq.nsn_decode_attention(p, q, cache["k"], cache["v"], cache["kr"], cache["vr"],
+                                      cache["table"], work, out_b, nq, r, scale)
+        torch.cuda.synchronize()
+        a, b = out_a.cpu().numpy(), out_b.cpu().numpy()
+        assert np.isfinite(a).all() and np.array_equal(a, b), (nq, r)
+    if rope:
+        with pytest.raises(ValueError):
+            call(128, 0)
+    with pytest.raises(nsnq.NsnError):
+        call(Nq + G, 0, q_pos=Nq + G)
