@@ -226,10 +226,15 @@ def nsn_build_codebook_workspace_size(sub_dim, n_samples, n_codes=256):
 
 
 def nsn_prepare_codebook(params, codebook, table, stream=None):
+    """Prepare `table` from `codebook` for `params`.  The tensor remembers the
+    sub-vector size and metadata layout it was prepared for (its contents
+    depend on both), and every call of this module that takes the table
+    refuses params that differ."""
     _dev(codebook, table)
     _lib.check(_lib.load().nsn_prepare_codebook(ctypes.byref(params.c), _ptr(codebook),
                                                 _ptr(table), table.numel() * table.element_size(),
                                                 _stream(stream)))
+    table._nsn_prepared_for = _table_key(params)
 
 
 def nsn_nearest_codeword(params, table, v, out, stream=None):
@@ -248,9 +253,17 @@ def nsn_nearest_codeword(params, table, v, out, stream=None):
                                                 _ptr(out), _stream(stream)))
 
 
+def _table_key(params):
+    return (params.sub_dim, params.dq)
+
+
 def _check_table(params, table):
     if table.numel() * table.element_size() < nsn_table_size(params):
         raise ValueError("table is smaller than nsn_table_size(params)")
+    made_for = getattr(table, "_nsn_prepared_for", None)
+    if made_for is not None and made_for != _table_key(params):
+        raise ValueError(f"table was prepared for (sub_dim, dq) = {made_for}, "
+                         f"used with {_table_key(params)}")
 
 
 def _check_codes(params, codes):

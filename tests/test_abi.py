@@ -396,6 +396,24 @@ def test_prepared_attention_checks_its_tensors_once():
         nsnq._check_attention_call(p, q.float(), plain, plain, kr, kr, table, work, out)
 
 
+def test_binding_refuses_a_table_prepared_for_other_params():
+    """A table tensor prepared through the binding carries the (sub_dim, dq)
+    it was made for; calls with other params are refused, an untagged table
+    is checked for its size only (host tensors, no GPU needed)."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    p4, p8, p4dq = nsnq.Params(sub_dim=4), nsnq.Params(sub_dim=8), nsnq.Params(sub_dim=4, dq=True)
+    table = torch.zeros(nsnq.nsn_table_size(p4), dtype=torch.uint8)
+    for p in (p4, p8, p4dq):
+        nsnq._check_table(p, table)
+    table._nsn_prepared_for = nsnq._table_key(p4)
+    nsnq._check_table(p4, table)
+    nsnq._check_table(nsnq.Params(sub_dim=4, group_size=256, scale_adjust=False), table)
+    for p in (p8, p4dq):
+        with pytest.raises(ValueError, match="prepared for"):
+            nsnq._check_table(p, table)
+
+
 def test_binding_checks_sequence_and_group_extents():
     """The C ABI trusts the sequence count and the group slots it is given:
     the binding rejects codes, meta or shift tensors with fewer sequences

@@ -374,3 +374,20 @@ def test_codebook_off_the_fp16_grid_is_rounded_once():
             dg = float(np.sum((vn[i] - Cr[got[i]]) ** 2))
             do = float(np.sum((vn[i] - Cr[want[i]]) ** 2))
             assert dg - do <= 1e-5 * max(do, 1e-12), (m, i)
+
+
+def test_table_prepared_for_other_params_is_refused():
+    """A table prepared through the binding is refused, before any launch,
+    by calls whose params need another table (1-bit codes, double-quantized
+    rounding); other params of the same sub-vector size use it."""
+    _say("table tag")
+    p, table, _ = table_for(4)
+    x = torch.zeros((1, 128, 128), dtype=torch.float16, device=DEV)
+    for bad in (nsnq.Params(sub_dim=8), nsnq.Params(sub_dim=4, dq=True)):
+        codes, meta, shift = (torch.zeros(sh, dtype=dt, device=DEV) for sh, dt in nsnq.cache_layout(bad, 1, 128))
+        with pytest.raises(ValueError, match="prepared for"):
+            nsnq.nsn_quantize(bad, x, table, codes, meta, shift)
+    ok = nsnq.Params(sub_dim=4, group_size=128, scale_adjust=False)
+    codes, meta, shift = alloc_outputs(1, 128, 4, 128)
+    nsnq.nsn_quantize(ok, x, table, codes, meta, shift)
+    torch.cuda.synchronize()
