@@ -155,10 +155,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-// byte K of w, times 2^S (a byte offset into the codebook)
-template <int K, int S>
+// byte K of w, times 2^S (a byte offset into the codebook).  The compiler
+// takes bytes 1-3 with one SDWA shift but byte 0 with a shift and a mask;
+// SDWA0 selects one SDWA shift for byte 0 too (the shift count sits in a
+// VGPR, hoisted out of the tile loop).  The rotary kernels keep the
+// compiler's form.
+template <int K, int S, bool SDWA0 = false>
 __device__ __forceinline__ uint32_t code_off(uint32_t w) {
-  return ((w >> (8 * K)) & 0xffu) << S;
+  if constexpr (K == 0 && SDWA0) {
+    uint32_t r;
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r)
+        : "v"(static_cast<uint32_t>(S)), "v"(w));
+    return r;
+  } else {
+    return ((w >> (8 * K)) & 0xffu) << S;
+  }
 }
 
 __device__ __forceinline__ v4f mfma16(const u32x4& a, const u32x4& b, const v4f& c) {
@@ -212,33 +224,33 @@ __device__ __forceinline__ u32x4 score_b(const typename TileData<M>::CT& kc, con
   const char* base = reinterpret_cast<const char*>(cbh);
   if constexpr (M == 4) {
     const uint32_t w = kc[S >> 1];
-    const u32x2 c0 = *reinterpret_cast<const u32x2*>(base + code_off<2 * (S & 1), 3>(w));
-    const u32x2 c1 = *reinterpret_cast<const u32x2*>(base + code_off<2 * (S & 1) + 1, 3>(w));
+    const u32x2 c0 = *reinterpret_cast<const u32x2*>(base + code_off<2 * (S & 1), 3, true>(w));
+    const u32x2 c1 = *reinterpret_cast<const u32x2*>(base + code_off<2 * (S & 1) + 1, 3, true>(w));
     return u32x4{c0.x, c0.y, c1.x, c1.y};
   } else {
-    return *reinterpret_cast<const u32x4*>(base + code_off<S, 4>(kc));
+    return *reinterpret_cast<const u32x4*>(base + code_off<S, 4, true>(kc));
   }
 }
 
 // Value A operand chunk of channel block CB for one token: channels
 // 4 (8a + CB) .. + 3 (a = lane % 4): code byte CB (m = 4) or half CB % 2 of
 // code byte CB / 2 (m = 8) of the lane's value-code bytes.
-template <int M, int CB>
+template <int M, int CB, bool SDWA0>
 __device__ __forceinline__ uint32_t value_chunk_off(const typename TileData<M>::CT& vc) {
   if constexpr (M == 4)
-    return code_off<CB & 3, 3>(vc[CB >> 2]);
+    return code_off<CB & 3, 3, SDWA0>(vc[CB >> 2]);
   else
-    return code_off<(CB >> 1), 4>(vc) + 8u * (CB & 1);
+    return code_off<(CB >> 1), 4, SDWA0>(vc) + 8u * (CB & 1);
 }
 
-template <int M, int CB>
+template <int M, int CB, bool SDWA0>
 __device__ __forceinline__ void value_steps(v4f (&acc)[8], const TileData<M>& d, int kb, const u32x4& bw,
                                             uint32_t cbh_base) {
   if constexpr (CB < 8) {
-    const uint2 a0 = ds_tr16(cbh_base + value_chunk_off<M, CB>(d.vc[2 * kb]));
-    const uint2 a1 = ds_tr16(cbh_base + value_chunk_off<M, CB>(d.vc[2 * kb + 1]));
+    const uint2 a0 = ds_tr16(cbh_base + value_chunk_off<M, CB, SDWA0>(d.vc[2 * kb]));
+    const uint2 a1 = ds_tr16(cbh_base + value_chunk_off<M, CB, SDWA0>(d.vc[2 * kb + 1]));
     acc[CB] = mfma16(u32x4{a0.x, a0.y, a1.x, a1.y}, bw, acc[CB]);
-    value_steps<M, CB + 1>(acc, d, kb, bw, cbh_base);
+    value_steps<M, CB + 1, SDWA0>(acc, d, kb, bw, cbh_base);
   }
 }
 
@@ -1029,7 +1041,7 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       const uint2 w0 = ds_tr16(wtr + (32 * kb) * 32);
       const uint2 w1 = ds_tr16(wtr + (32 * kb + 4) * 32);
       const u32x4 bw = u32x4{w0.x, w0.y, w1.x, w1.y};
-      value_steps<M, 0>(acc, d, kb, bw, cbh_base);
+      value_steps<M, 0, !ROPE>(acc, d, kb, bw, cbh_base);
     }
     if constexpr (!ROPE) __builtin_amdgcn_s_setprio(0);
     if (more) load_values<M>(d, vcrow + tn * kTile * CB, voff);
