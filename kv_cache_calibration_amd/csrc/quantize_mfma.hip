@@ -90,20 +90,45 @@ __device__ __forceinline__ float fma_f16(uint32_t w, float ns, float z) {
   return d;
 }
 
-// ||z - s c||^2 for codeword `code` of the fp16 codebook in LDS, ns = -s.
-// With z = s h this is s^2 ||h - c||^2: the same order over codewords as the
-// distance to h, without forming h.
-__device__ __forceinline__ float sqdist_cb(const float (&z)[4], const uint32_t* cbh, uint32_t code,
+// The shift count 3 in a VGPR that the compiler cannot rematerialize: made
+// once per kernel, so the SDWA shifts below share one register instead of a
+// fresh constant move each.
+__device__ __forceinline__ uint32_t vgpr_three() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, 3" : "=v"(r));
+  return r;
+}
+
+// 8 x byte i of w: the byte offset in the fp16 codebook of the code held in
+// that byte.  The compiler takes bytes 1-3 with one SDWA shift but byte 0
+// with a shift and a mask; byte 0 goes through one SDWA shift here as well
+// (three = vgpr_three()).
+__device__ __forceinline__ uint32_t code_byte_off(uint32_t w, int i, uint32_t three) {
+  if (i == 0) {
+    uint32_t r;
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r)
+        : "v"(three), "v"(w));
+    return r;
+  }
+  return ((w >> (8 * i)) & 0xffu) << 3;
+}
+
+// ||z - s c||^2 for the codeword at byte offset `off` (8 x its code) of the
+// fp16 codebook in LDS, ns = -s.  With z = s h this is s^2 ||h - c||^2: the
+// same order over codewords as the distance to h, without forming h.
+__device__ __forceinline__ float sqdist_cb(const float (&z)[4], const uint32_t* cbh, uint32_t off,
                                            float ns) {
-  const uint2 w = *reinterpret_cast<const uint2*>(&cbh[2 * code]);
+  const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cbh) + off);
   const float d0 = fma_f16<0>(w.x, ns, z[0]), d1 = fma_f16<1>(w.x, ns, z[1]);
   const float d2 = fma_f16<0>(w.y, ns, z[2]), d3 = fma_f16<1>(w.y, ns, z[3]);
   return fmaf(d3, d3, fmaf(d2, d2, fmaf(d1, d1, d0 * d0)));
 }
 
-// codeword `code` of the fp16 codebook in LDS, as fp32 (exact)
-__device__ __forceinline__ void codeword(const uint32_t* cbh, uint32_t code, float (&cv)[4]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(&cbh[2 * code]);
+// the codeword at byte offset `off` (8 x its code) of the fp16 codebook in
+// LDS, as fp32 (exact)
+__device__ __forceinline__ void codeword(const uint32_t* cbh, uint32_t off, float (&cv)[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cbh) + off);
   const h2v a = __builtin_bit_cast(h2v, w.x), b = __builtin_bit_cast(h2v, w.y);
   cv[0] = static_cast<float>(a.x);
   cv[1] = static_cast<float>(a.y);
@@ -397,6 +422,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   // entry may be resolved at any later point).
   uint8_t* resb = reinterpret_cast<uint8_t*>(&res[w][0][0]);   // lane l: bytes 16 l .. 16 l + 15
   QEntry* ring = reinterpret_cast<QEntry*>(&fs.xs[w][0]);
+  const uint32_t three = vgpr_three();
   int qhead = 0, qtail = 0;   // wave-uniform ring positions
   auto flush = [&](int n) {
     wave_lds_sync();
@@ -409,7 +435,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
-        const float d = sqdist_cb(e.h, cbh, code, e.ns);
+        const float d = sqdist_cb(e.h, cbh, code_byte_off(e.codes, i, three), e.ns);
         bc = d < bd ? code : bc;
         bd = d < bd ? d : bd;
       }
@@ -443,8 +469,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       uint32_t best = 0xffffffffu;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t code = (asc >> (8 * i)) & 0xffu;
-        const float d = sqdist_cb(hv, cbh, code, nsc);
+        const float d = sqdist_cb(hv, cbh, code_byte_off(asc, i, three), nsc);
         best = min(best, (__float_as_uint(d) & ~3u) | static_cast<uint32_t>(i));
       }
       const uint32_t bc = (asc >> (8 * (best & 3u))) & 0xffu;
@@ -487,7 +512,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
           for (int r = 0; r < kCodes / kWave; ++r) {
             const uint32_t code = static_cast<uint32_t>(lane + kWave * r);
-            const float d = sqdist_cb(hv, cbh, code, ns);
+            const float d = sqdist_cb(hv, cbh, code << 3, ns);
             bc = d < bd ? code : bc;
             bd = d < bd ? d : bd;
           }
@@ -514,9 +539,8 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int mb = k >> 2, q = k & 3;
-    const uint32_t code = (codes4[mb] >> (8 * q)) & 0xffu;
     float cv[4];
-    codeword(cbh, code, cv);
+    codeword(cbh, code_byte_off(codes4[mb], q, three), cv);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       dot = fmaf(acc[mb][4 * q + e], cv[e], dot);
