@@ -64,7 +64,7 @@ struct alignas(16) QEntry {
   uint32_t codes;  // candidates five to eight, ascending
   float best;      // best distance among the first four
   uint32_t dst;    // byte of the owner's result row
-  float ns;        // -s2 of the owner's token
+  float s;         // s2 of the owner's token (1 when it is 0)
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -75,18 +75,18 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
-// h - c for c the low (HI = 0) or high (HI = 1) fp16 half of w: one
-// v_fma_mix_f32 (h + (-1) c with c widened exactly), rounded like the fp32
-// subtraction.  Arithmetic only.
-// z + ns c for c the low (HI = 0) or high (HI = 1) fp16 half of w: one
-// v_fma_mix_f32 (c widened exactly).  Arithmetic only.
+// z - s c for c the low (HI = 0) or high (HI = 1) fp16 half of w: one
+// v_fma_mix_f32 (c widened exactly, s negated by the source modifier, one
+// rounding).  Arithmetic only.
 template <int HI>
-__device__ __forceinline__ float fma_f16(uint32_t w, float ns, float z) {
+__device__ __forceinline__ float fma_f16(uint32_t w, float s, float z) {
   float d;
   if constexpr (HI)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(ns), "v"(z));
+    asm("v_fma_mix_f32 %0, %1, -%2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(d) : "v"(w), "v"(s), "v"(z));
   else
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(ns), "v"(z));
+    asm("v_fma_mix_f32 %0, %1, -%2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(d) : "v"(w), "v"(s), "v"(z));
   return d;
 }
 
@@ -100,28 +100,34 @@ __device__ __forceinline__ uint32_t vgpr_three() {
 }
 
 // 8 x byte i of w: the byte offset in the fp16 codebook of the code held in
-// that byte.  The compiler takes bytes 1-3 with one SDWA shift but byte 0
-// with a shift and a mask; byte 0 goes through one SDWA shift here as well
-// (three = vgpr_three()).
+// that byte, by one SDWA shift (three = vgpr_three()).  The compiler forms
+// bytes 1-3 that way with a constant register of its own but byte 0 with a
+// shift and a mask; all four go through the one shared register here.
 __device__ __forceinline__ uint32_t code_byte_off(uint32_t w, int i, uint32_t three) {
-  if (i == 0) {
-    uint32_t r;
+  uint32_t r;
+  if (i == 0)
     asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
-        : "=v"(r)
-        : "v"(three), "v"(w));
-    return r;
-  }
-  return ((w >> (8 * i)) & 0xffu) << 3;
+        : "=v"(r) : "v"(three), "v"(w));
+  else if (i == 1)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(three), "v"(w));
+  else if (i == 2)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(three), "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(three), "v"(w));
+  return r;
 }
 
 // ||z - s c||^2 for the codeword at byte offset `off` (8 x its code) of the
-// fp16 codebook in LDS, ns = -s.  With z = s h this is s^2 ||h - c||^2: the
-// same order over codewords as the distance to h, without forming h.
+// fp16 codebook in LDS.  With z = s h this is s^2 ||h - c||^2: the same order
+// over codewords as the distance to h, without forming h.
 __device__ __forceinline__ float sqdist_cb(const float (&z)[4], const uint32_t* cbh, uint32_t off,
-                                           float ns) {
+                                           float s) {
   const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(cbh) + off);
-  const float d0 = fma_f16<0>(w.x, ns, z[0]), d1 = fma_f16<1>(w.x, ns, z[1]);
-  const float d2 = fma_f16<0>(w.y, ns, z[2]), d3 = fma_f16<1>(w.y, ns, z[3]);
+  const float d0 = fma_f16<0>(w.x, s, z[0]), d1 = fma_f16<1>(w.x, s, z[1]);
+  const float d2 = fma_f16<0>(w.y, s, z[2]), d3 = fma_f16<1>(w.y, s, z[3]);
   return fmaf(d3, d3, fmaf(d2, d2, fmaf(d1, d1, d0 * d0)));
 }
 
@@ -388,7 +394,6 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
   // The search runs on z = s2 h directly: distances ||z - s2 c||^2 and bins
   // of z / s2.  A zero z (s2 = 0) is h = 0: scale 1 gives the same answer.
   const float sc = s2 > 0.f ? s2 : 1.0f;
-  const float nsc = -sc;
   const float fine_scale = kFineInv / sc;
 
   // ---- nearest codeword, four sub-vectors (one mb block) per step; the
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t code = (e.codes >> (8 * i)) & 0xffu;
-        const float d = sqdist_cb(e.h, cbh, code_byte_off(e.codes, i, three), e.ns);
+        const float d = sqdist_cb(e.h, cbh, code_byte_off(e.codes, i, three), e.s);
         bc = d < bd ? code : bc;
         bd = d < bd ? d : bd;
       }
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
       uint32_t best = 0xffffffffu;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float d = sqdist_cb(hv, cbh, code_byte_off(asc, i, three), nsc);
+        const float d = sqdist_cb(hv, cbh, code_byte_off(asc, i, three), sc);
         best = min(best, (__float_as_uint(d) & ~3u) | static_cast<uint32_t>(i));
       }
       const uint32_t bc = (asc >> (8 * (best & 3u))) & 0xffu;
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
         e.codes = hi;
         e.best = __uint_as_float(best & ~3u);
         e.dst = dst;
-        e.ns = nsc;
+        e.s = sc;
         ring[(qtail + __popcll(bq & below)) & (kRing - 1)] = e;
       }
       qtail += __popcll(bq);
@@ -506,13 +511,13 @@ __global__ __launch_bounds__(kG * 2, 2) void quantize_mfma_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             hv[e] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[mb][4 * q + e]), src));
-          const float ns = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nsc), src));
+          const float ss = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), src));
           float bd = __builtin_huge_valf();
           uint32_t bc = 0;
 #pragma unroll
           for (int r = 0; r < kCodes / kWave; ++r) {
             const uint32_t code = static_cast<uint32_t>(lane + kWave * r);
-            const float d = sqdist_cb(hv, cbh, code << 3, ns);
+            const float d = sqdist_cb(hv, cbh, code << 3, ss);
             bc = d < bd ? code : bc;
             bd = d < bd ? d : bd;
           }
