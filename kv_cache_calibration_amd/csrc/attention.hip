@@ -311,10 +311,15 @@ __device__ __forceinline__ v8h hblk(const HOps& o, int a, int kb) {
 __device__ __forceinline__ uint32_t f16_hi2(float z0, float z1) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(z0, z1));
 }
+// The result feeds matrix-core operands.  A VALU write of a VGPR needs two
+// wait states before an MFMA reads it; the compiler inserts them after its
+// own VALU instructions but does not count an inline-asm instruction as
+// such a write, so the asm block ends with them.
 __device__ __forceinline__ uint32_t f16_lo2(float z0, float z1, uint32_t hi) {
   uint32_t l;
   asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[0,0,1]" : "=v"(l) : "v"(z0), "v"(hi));
-  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(l) : "v"(z1), "v"(hi));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\ts_nop 1"
+      : "+v"(l) : "v"(z1), "v"(hi));
   return l;
 }
 
