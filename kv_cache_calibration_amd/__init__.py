@@ -40,6 +40,7 @@ __all__ = [
     "nsn_decode_attention_noalloc",
     "nsn_decode_attention_workspace_size",
     "PreparedDecodeAttention",
+    "PreparedResidualAppend",
     "lib_path",
     "cache_layout",
 ]
@@ -324,8 +325,7 @@ def nsn_dequantize(params, codes, meta, shift, table, out, n_tok=None, stream=No
                                   _stream(stream)))
 
 
-def nsn_residual_append(tok, resid, pos, stream=None):
-    """tok fp16 (n_seq, 128); resid fp16 (n_seq, cap, 128)."""
+def _check_append(tok, resid):
     _dev(tok, resid)
     import torch
     if not tok.is_contiguous():
@@ -333,9 +333,34 @@ def nsn_residual_append(tok, resid, pos, stream=None):
     if tok.dtype != torch.float16 or resid.dtype != torch.float16 or tuple(tok.shape) != (resid.shape[0], 128):
         raise ValueError("tok must be fp16 (n_seq, 128) and resid fp16 (n_seq, cap, 128)")
     _inner_contig(resid, (resid.shape[1], 128))
+
+
+def nsn_residual_append(tok, resid, pos, stream=None):
+    """tok fp16 (n_seq, 128); resid fp16 (n_seq, cap, 128)."""
+    _check_append(tok, resid)
     lib = _lib.load()
     _lib.check(lib.nsn_residual_append(_ptr(tok), tok.shape[0], _ptr(resid), resid.stride(0),
                                        resid.shape[1], pos, _stream(stream)))
+
+
+class PreparedResidualAppend:
+    """nsn_residual_append with its tensors checked and marshalled once, for a
+    decode loop that writes each step's token into the same buffer `tok`.
+    Calling the object with the step's residual slot makes the library call
+    (which still validates every argument); the object holds references to
+    the tensors, which must keep their shapes.  Results equal those of the
+    per-call function."""
+
+    def __init__(self, tok, resid):
+        _check_append(tok, resid)
+        self._keep = (tok, resid)
+        self._fn = _lib.load().nsn_residual_append
+        self._head = (_ptr(tok), tok.shape[0], _ptr(resid), resid.stride(0), resid.shape[1])
+
+    def __call__(self, pos, stream=None):
+        status = self._fn(*self._head, pos, _stream(stream))
+        if status != _lib.NSN_OK:
+            _lib.check(status)
 
 
 def _shape(batch, n_q_heads, n_kv_heads, n_quant_tok, n_resid_tok, cache_capacity,

@@ -414,6 +414,17 @@ def test_binding_refuses_a_table_prepared_for_other_params():
             nsnq._check_table(p, table)
 
 
+def test_prepared_append_checks_its_tensors_once():
+    """PreparedResidualAppend runs the per-call function's checks at
+    construction: host tensors are refused before anything is marshalled."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_calibration_amd as nsnq
+    tok = torch.zeros((4, 128), dtype=torch.float16)
+    resid = torch.zeros((4, 16, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device"):
+        nsnq.PreparedResidualAppend(tok, resid)
+
+
 def test_binding_checks_sequence_and_group_extents():
     """The C ABI trusts the sequence count and the group slots it is given:
     the binding rejects codes, meta or shift tensors with fewer sequences

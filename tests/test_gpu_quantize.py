@@ -242,6 +242,27 @@ def test_residual_append_writes_the_slot():
     assert not r[:, :7].any() and not r[:, 8:].any()
 
 
+def test_prepared_residual_append_matches_per_call():
+    """A decode loop writing each step's token into one buffer and appending
+    it through PreparedResidualAppend fills the window as the per-call
+    function does; a slot past the capacity is refused by the library."""
+    n_seq, cap = 7, 12
+    toks = torch.randn((cap, n_seq, 128), dtype=torch.float16, device=DEV)
+    a = torch.full((n_seq, cap, 128), float("nan"), dtype=torch.float16, device=DEV)
+    b = a.clone()
+    buf = torch.empty((n_seq, 128), dtype=torch.float16, device=DEV)
+    append = nsnq.PreparedResidualAppend(buf, b)
+    for t in range(cap):
+        nsnq.nsn_residual_append(toks[t], a, t)
+        buf.copy_(toks[t])
+        append(t)
+    torch.cuda.synchronize()
+    assert torch.equal(a.cpu(), b.cpu())
+    assert torch.equal(b.cpu().transpose(0, 1), toks.cpu())
+    with pytest.raises(nsnq.NsnError):
+        append(cap)
+
+
 def test_quantize_prefill_full_size_sampled():
     """The prefill workload at full size in the launch the benchmark times:
     2048 sequences (32 layers x batch 4 x 8 kv heads, K and V) x 131072 fp16
