@@ -294,8 +294,10 @@ nsn_status nsn_residual_append(const uint16_t* tok, int64_t n_seq,
                                void* stream);
 
 typedef struct {
-  int32_t batch;          /* B */
-  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads */
+  int32_t batch;          /* B, at most 65535 (else NSN_ERR_UNSUPPORTED) */
+  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads; Hkv * Hq at most
+                             2^20 and Hkv * ceil(Hq / Hkv / 4) at most 65535
+                             (else NSN_ERR_UNSUPPORTED) */
   int32_t n_kv_heads;     /* Hkv; q head h reads kv head h / (Hq/Hkv) */
   int32_t n_quant_tok;    /* quantized tokens per (b, kv head); multiple of G */
   int32_t n_resid_tok;    /* valid fp16 residual tokens, 0..resid_capacity */

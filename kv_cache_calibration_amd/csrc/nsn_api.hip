@@ -326,6 +326,10 @@ static nsn_status check_attn(const nsn_params* p, const nsn_attn_shape* s) {
     return fail(NSN_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
   if (s->batch > 65535 || static_cast<int64_t>(s->n_kv_heads) * s->n_q_heads > (1 << 20))
     return fail(NSN_ERR_UNSUPPORTED, "batch or head count too large");
+  // the split launch's second grid dimension: one workgroup row per (kv
+  // head, block of up to four of its query heads), at most 65535
+  if (static_cast<int64_t>(s->n_kv_heads) * ((s->n_q_heads / s->n_kv_heads + 3) / 4) > 65535)
+    return fail(NSN_ERR_UNSUPPORTED, "too many (kv head, query-head block) rows for one launch");
   if (s->n_quant_tok < 0 || s->n_resid_tok < 0)
     return fail(NSN_ERR_INVALID_ARG, "token counts must be >= 0");
   if (s->n_quant_tok + static_cast<int64_t>(s->n_resid_tok) < 1)

@@ -168,6 +168,10 @@ def _shape(**kw):
     (dict(softmax_scale=0.0), _lib.NSN_ERR_INVALID_ARG),
     (dict(batch=0), _lib.NSN_ERR_INVALID_ARG),
     (dict(n_resid_tok=2000, resid_capacity=4096), _lib.NSN_ERR_UNSUPPORTED),
+    (dict(batch=65536), _lib.NSN_ERR_UNSUPPORTED),
+    # one kv head with 2^18 query heads: 65536 rows of head blocks, one more
+    # than a launch's second grid dimension holds
+    (dict(n_q_heads=1 << 18, n_kv_heads=1), _lib.NSN_ERR_UNSUPPORTED),
 ])
 def test_attention_validation(lib, kw, status):
     s = _shape(**kw)
