@@ -287,6 +287,7 @@ nsn_status nsn_dequantize(const nsn_params* p, const uint8_t* codes,
  * tok    device fp16 [n_seq][128] (contiguous).
  * resid  device fp16, token t of sequence s at resid + s*resid_seq_stride
  *        + t*128; requires 0 <= pos < resid_capacity.
+ * n_seq above 2^28 - 16 (one launch) returns NSN_ERR_UNSUPPORTED.
  */
 nsn_status nsn_residual_append(const uint16_t* tok, int64_t n_seq,
                                uint16_t* resid, int64_t resid_seq_stride,

@@ -41,6 +41,7 @@ nsn_status hip_status(hipError_t e, const char* what) {
 // 256 threads per workgroup) must stay below 2^32.
 constexpr int64_t kMaxGroups = (int64_t(1) << 24) - 1;     // workgroup per token group
 constexpr int64_t kMaxNearest = (int64_t(1) << 32) - 256;  // one work-item per sub-vector
+constexpr int64_t kMaxAppendSeq = (int64_t(1) << 28) - 16;  // 16 work-items per sequence
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 // The shift argument: 16 bytes, or 8 with NSN_DQ (the 136-byte group records
@@ -309,6 +310,8 @@ nsn_status nsn_residual_append(const uint16_t* tok, int64_t n_seq, uint16_t* res
   if (!tok || !resid) return fail(NSN_ERR_INVALID_ARG, "tok and resid must be non-NULL");
   if (!aligned16(tok) || !aligned16(resid))
     return fail(NSN_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (n_seq > kMaxAppendSeq)   // 16 work-items per sequence in one launch
+    return fail(NSN_ERR_UNSUPPORTED, "n_seq above %lld", static_cast<long long>(kMaxAppendSeq));
   if (n_seq > 1 && (resid_seq_stride < resid_capacity * 128 || resid_seq_stride % 8))
     return fail(NSN_ERR_INVALID_ARG,
                 "resid_seq_stride must be >= resid_capacity*128 and a multiple of 8");

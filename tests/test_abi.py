@@ -150,6 +150,8 @@ def test_prepare_and_append_validation(lib):
     assert a(FAKE, 4, FAKE, 128 * 128, 128, -1, NULL) == _lib.NSN_ERR_INVALID_ARG
     assert a(FAKE, 4, FAKE, 100, 128, 3, NULL) == _lib.NSN_ERR_INVALID_ARG  # stride too small
     assert a(NULL, 0, NULL, 0, 128, 3, NULL) == _lib.NSN_OK
+    # more sequences than one launch's 2^32 work-items cover (16 per sequence)
+    assert a(FAKE, 1 << 28, FAKE, 128 * 128, 128, 3, NULL) == _lib.NSN_ERR_UNSUPPORTED
 
 
 def _shape(**kw):
