@@ -825,23 +825,24 @@ __global__ __launch_bounds__(kThreads, ROPE ? 2 : kBlocksPerCU) void attn_split_
       // v < 4 channel 32pm + 8q + 4hA + v, v >= 4 the same channel + 64 (the
       // key operand below uses the same order).  Kept in LDS (registers are
       // the limit here); lanes of rows 8..31 read a copy of row l % 8, whose
-      // output rows are never used.
+      // output rows are never used.  The 128 entries (8 rows x 8 slices x 2
+      // lane halves) are made by the whole wave, two per lane: lane l takes
+      // row l % 8, half (l / 8) % 2 and slices l / 16 and l / 16 + 4.
       {
-        const int row = lane & 31, hA = lane >> 5;
-        const int hq = row & 3, part = row >> 2;
-        if (row < 8)
+        const int row = lane & 7, hA = (lane >> 3) & 1, sp = lane >> 4;
+        const int hq = row & 3;
+        const bool lo_part = row >= 4;
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
+        for (int j = 0; j < 2; ++j) {
+          const int sl = sp + 4 * j;
           const int c = 32 * (sl >> 2) + 8 * (sl & 3) + 4 * hA;
           const float4 u = *reinterpret_cast<const float4*>(&rsm.qp[wave][hq][c]);
           const float4 v = *reinterpret_cast<const float4*>(&rsm.qp[wave][hq][c + kD / 2]);
           uint32_t w4[4] = {f16_hi2(u.x, u.y), f16_hi2(u.z, u.w), f16_hi2(v.x, v.y), f16_hi2(v.z, v.w)};
-          if (part == 1) {
-            w4[0] = f16_lo2(u.x, u.y, w4[0]);
-            w4[1] = f16_lo2(u.z, u.w, w4[1]);
-            w4[2] = f16_lo2(v.x, v.y, w4[2]);
-            w4[3] = f16_lo2(v.z, v.w, w4[3]);
-          }
+          const uint32_t l4[4] = {f16_lo2(u.x, u.y, w4[0]), f16_lo2(u.z, u.w, w4[1]),
+                                  f16_lo2(v.x, v.y, w4[2]), f16_lo2(v.z, v.w, w4[3])};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w4[i] = lo_part ? l4[i] : w4[i];
           rsm.qkl[wave][sl][hA][row] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
         wave_lds_sync();
